@@ -1,0 +1,171 @@
+"""fp64 CPU oracle for the NSA forward pass and the selection-branch gradient.
+
+TEST INFRASTRUCTURE ONLY.  This package is the independent reference that the
+HIP library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import it.  It shares no code with
+the HIP library (``sparse_attention_long_compress_amd``) and imports nothing
+from it; the product path never calls it.
+
+The arithmetic lives in ``nsa_oracle.c`` (plain C, double precision, OpenMP
+across independent rows).  This module only builds that file with gcc, loads it
+with ctypes and marshals numpy arrays.  Every function takes and returns
+float64 arrays; bf16 inputs are widened to float64 exactly by the caller.
+
+Parity-pin status (what pins each function; see tests/test_oracle_pins.py):
+  pool              constant block, arithmetic-progression closed form
+  forward/o_cmp     constant keys (uniform weights, closed form), torch fp64
+                    SDPA over avg-pooled keys with a block-causal mask
+  forward/indices   all-ties closed form, brute-force subset enumeration,
+                    numpy stable argsort, P:53 sparsity arithmetic
+  forward/o_sel     full causal attention when top-k covers all blocks (torch
+                    SDPA), explicit-mask SDPA given the index table
+  forward/o_win     W >= T full causal, W = 1 returns v_t, banded-mask SDPA
+  forward/out       zero gates, unit gates, linearity, shift invariances
+  select_bwd        central finite differences, torch autograd of causal and
+                    masked SDPA
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libnsa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile nsa_oracle.c into libnsa_oracle.so next to it (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-std=c99", "-Wall", "-shared", "-fPIC",
+             _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+        ):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        ci = ctypes.c_int
+        lib.nsa_oracle_pool.argtypes = [ci, ci, ci, ci, ci, dp, dp]
+        lib.nsa_oracle_pool.restype = ci
+        lib.nsa_oracle_forward.argtypes = (
+            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [dp] * 5 + [ip, ci, dp, dp, ci]
+        )
+        lib.nsa_oracle_forward.restype = ci
+        lib.nsa_oracle_select_bwd.argtypes = (
+            [ci] * 7 + [ctypes.c_double] + [dp] * 4 + [ip, dp, dp, dp, dp, ci]
+        )
+        lib.nsa_oracle_select_bwd.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _dptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def default_threads() -> int:
+    return int(os.environ.get("NSA_ORACLE_THREADS", "0")) or (os.cpu_count() or 1)
+
+
+def pool(x, blk: int = 64):
+    """Mean-pool [B,T,H,D] over non-overlapping complete blocks -> [B,T//blk,H,D]."""
+    x = _f64(x)
+    B, T, H, D = x.shape
+    out = np.zeros((B, T // blk, H, D), dtype=np.float64)
+    rc = _load().nsa_oracle_pool(B, T, H, D, blk, _dptr(x), _dptr(out))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_pool failed: {rc}")
+    return out
+
+
+def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: float | None = None,
+            indices=None, want_scores: bool = False, threads: int | None = None):
+    """Full NSA forward.  Returns a dict of float64/int32 numpy arrays:
+    out, o_cmp, o_sel, o_win [B,T,Hq,D]; lse_sel [B,Hq,T]; indices [B,Hkv,T,top_k];
+    gap [B,Hkv,T]; scores [B,Hkv,T,nblk] (when want_scores).
+
+    ``indices`` (optional, int32) freezes the selection to a table the oracle
+    produced earlier instead of running the top-k step."""
+    q, k, v, gates = _f64(q), _f64(k), _f64(v), _f64(gates)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    nblk = -(-T // blk)
+    res = {
+        "out": np.zeros((B, T, Hq, D)),
+        "o_cmp": np.zeros((B, T, Hq, D)),
+        "o_sel": np.zeros((B, T, Hq, D)),
+        "o_win": np.zeros((B, T, Hq, D)),
+        "lse_sel": np.zeros((B, Hq, T)),
+        "gap": np.zeros((B, Hkv, T)),
+    }
+    if indices is not None:
+        idx = np.ascontiguousarray(np.asarray(indices, dtype=np.int32)).copy()
+        assert idx.shape == (B, Hkv, T, top_k)
+    else:
+        idx = np.zeros((B, Hkv, T, top_k), dtype=np.int32)
+    res["indices"] = idx
+    scores = np.zeros((B, Hkv, T, nblk)) if want_scores else None
+    rc = _load().nsa_oracle_forward(
+        B, T, Hq, Hkv, D, blk, top_k, window, float(scale),
+        _dptr(q), _dptr(k), _dptr(v), _dptr(gates),
+        _dptr(res["out"]), _dptr(res["o_cmp"]), _dptr(res["o_sel"]), _dptr(res["o_win"]),
+        _dptr(res["lse_sel"]), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        1 if indices is not None else 0, _dptr(scores), _dptr(res["gap"]),
+        threads if threads is not None else default_threads())
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_forward failed: {rc}")
+    if want_scores:
+        res["scores"] = scores
+    return res
+
+
+def select_bwd(q, k, v, gates, indices, dout, *, top_k: int, blk: int = 64,
+               scale: float | None = None, threads: int | None = None):
+    """Gradient of the selection branch (indices and gates frozen).
+    Returns (dq [B,T,Hq,D], dk [B,T,Hkv,D], dv [B,T,Hkv,D]) in float64."""
+    q, k, v, gates, dout = _f64(q), _f64(k), _f64(v), _f64(gates), _f64(dout)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    idx = np.ascontiguousarray(np.asarray(indices, dtype=np.int32))
+    assert idx.shape == (B, Hkv, T, top_k)
+    dq = np.zeros((B, T, Hq, D))
+    dk = np.zeros((B, T, Hkv, D))
+    dv = np.zeros((B, T, Hkv, D))
+    rc = _load().nsa_oracle_select_bwd(
+        B, T, Hq, Hkv, D, blk, top_k, float(scale),
+        _dptr(q), _dptr(k), _dptr(v), _dptr(gates),
+        idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _dptr(dout),
+        _dptr(dq), _dptr(dk), _dptr(dv),
+        threads if threads is not None else default_threads())
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_select_bwd failed: {rc}")
+    return dq, dk, dv
