@@ -1,0 +1,180 @@
+"""Throughput benchmark of the MI355X NSA forward (one GPU).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                [--no-cpu-baseline] [--profile-only]
+
+A step is one whole forward pass (pool, compressed attention + top-k,
+selection + window + gated combine) over one batch of seeded synthetic input
+already resident in HBM.  Prints ONE JSON line (rank 0, N = 1):
+  value      = tokens/s = batch * seq_len / (seconds per step)
+  roofline   = the selection/window/combine kernel (the dominant one): useful
+               attention FLOPs per launch / its average duration, measured with
+               HIP events recorded around it on its own stream in every timed
+               step, against the bf16 dense MFMA peak
+  cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
+               same workload (query rows spread evenly over the sequence)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NSA fwd tokens/sec at seq 8192 GQA-4 bf16; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def useful_counts(wl):
+    """Per (b, h): sums over t of |K_sel(t)|, |K_win(t)|, n_c(t) -- the keys the
+    method itself must attend (closed form of the selection rules)."""
+    T, k, W = wl.seq_len, wl.top_k, wl.window
+    sel = win = cmp = 0
+    for t in range(T):
+        c = t // 64
+        if c == 0:
+            sel += t + 1
+        else:
+            sel += (t % 64 + 1) + 64 + 64 * min(c - 1, k - 2)
+        win += min(W, t + 1)
+        cmp += (t + 1) // 64
+    return sel, win, cmp
+
+
+def useful_flops(wl):
+    sel, win, cmp = useful_counts(wl)
+    per = 4 * wl.head_dim * wl.batch * wl.n_q_heads
+    return {"sel_win": per * (sel + win), "cmp": per * cmp, "total": per * (sel + win + cmp)}
+
+
+def algorithmic_bytes(wl):
+    """HBM bytes the whole forward must move at least once (inputs read once,
+    output written once)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    B, T, Hq, Hkv, D = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    return es * (B * T * Hq * D * 2 + 2 * B * T * Hkv * D + B * T * Hq * 3)
+
+
+def cpu_baseline(wl, arrs_f64, budget_rows=None):
+    import numpy as np
+
+    import oracle
+
+    threads = int(os.environ.get("NSA_ORACLE_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    T = wl.seq_len
+    n = budget_rows or min(T, 1024)
+    rows = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.forward(arrs_f64["q"], arrs_f64["k"], arrs_f64["v"], arrs_f64["gates"],
+                   top_k=wl.top_k, window=wl.window, scale=wl.scale, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(wl.batch * len(rows) / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {T} query positions (evenly spaced) x batch {wl.batch}, "
+                      f"all heads, fp64, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="340m-gqa4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup + steps and exit without the oracle (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over batch or KV groups with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_compress_amd as nsa
+    from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64, draw, to_dtype
+
+    wl = WORKLOADS[args.workload]
+    arrs = draw(wl)
+    cpu = to_dtype(arrs, wl.dtype)
+    dev = {k: v.to("cuda") for k, v in cpu.items()}
+    del arrs
+    p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale)
+    ws = nsa.alloc_workspace(p, dev["q"].device)
+    out = torch.empty_like(dev["q"])
+
+    def step(events=None):
+        nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                    window=wl.window, scale=wl.scale, out=out, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # events (created by torch on the current stream's device; raw handles go to the library)
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in row:
+            e.record()  # materialise the underlying hipEvent_t
+        evs.append(row)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events=[e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
+    k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
+    k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
+    ev_step = np.mean([r[0].elapsed_time(r[3]) for r in evs]) * 1e-3
+    fl = useful_flops(wl)
+    tokens = wl.batch * wl.seq_len
+    if args.profile_only:
+        print(json.dumps({"profile_only": True, "ms_per_step": wall * 1e3,
+                          "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6}), flush=True)
+        return
+
+    achieved = fl["sel_win"] / k3 / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(tokens / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, sigmoid(N(0,1)) gates)",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "block": 64, "top_k": wl.top_k,
+                   "window": wl.window, "parallelism": "none (1 GPU)"},
+        "useful_tflops": round(fl["total"] / wall / 1e12, 2),
+        "pct_bf16_peak": round(100 * fl["total"] / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "stage_us": {"pool": round(k1 * 1e6, 2), "cmp_select": round(k2 * 1e6, 2),
+                     "sel_win_combine": round(k3 * 1e6, 2), "events_total": round(ev_step * 1e6, 2)},
+        "roofline": {"kernel": "sel_win_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        f64 = {k: as_f64(v) for k, v in cpu.items()}
+        res["cpu_baseline"] = cpu_baseline(wl, f64)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

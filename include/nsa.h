@@ -1,0 +1,179 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) Native Sparse Attention library.
+ *
+ * The operation: causal GQA prefill attention with three branches mixed by
+ * per-head gates, as described on the pages
+ *   [DSA] "DeepSeek's Native Sparse Attention" (newsletter #44), section
+ *         "How Does Native Sparse Attention Work?": COMPRESSION, SELECTION and
+ *         SLIDING WINDOW bullets and the gate paragraph that follows them;
+ *   [SIC] "Sparsity is Cool: Reverse-Engineering MoBA and NSA" (wiki summary),
+ *         section Method (mean-pool compression, block 64, top-k 16, window
+ *         512) and Key claims (the first block is always selected; the
+ *         two-pass query- plus key/value-stationary selection backward).
+ *
+ * For query position t (0-based), query head h, KV group g = h / (Hq/Hkv):
+ *   compression : Kc_j, Vc_j = mean of the 64 keys/values of block j
+ *                 (non-overlapping, complete blocks only);
+ *                 o_cmp = softmax_j(tau q.Kc_j) Vc over j < floor((t+1)/64),
+ *                 o_cmp = 0 when no block is complete yet;
+ *   importance  : S_j(t,g) = sum over the heads of g of the compressed
+ *                 attention probabilities;
+ *   selection   : I(t,g) = {0, own = t/64} plus the (top_k - |forced|) blocks
+ *                 of 1..own-1 with the largest S (ties: lower index); all of
+ *                 them when there are no more than that; o_sel = softmax
+ *                 attention over the tokens s <= t of the blocks in I;
+ *   window      : o_win = softmax attention over t-W < s <= t;
+ *   output      : out = g_cmp o_cmp + g_sel o_sel + g_win o_win.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *   - Layouts are row-major and contiguous:
+ *       q, out, o_sel, dout, dq : [B][T][Hq][D]
+ *       k, v, dk, dv            : [B][T][Hkv][D]
+ *       gates                   : [B][T][Hq][3]   (g_cmp, g_sel, g_win)
+ *       indices                 : int32 [B][Hkv][T][top_k], ascending, -1 pad
+ *       lse_sel                 : float [B][Hq][T], natural log
+ *       k_cmp, v_cmp            : [B][T/64][Hkv][D]
+ *     Element type of q/k/v/gates/out/o_sel/dout/dq/dk/dv/k_cmp/v_cmp is
+ *     params->dtype (bf16 or fp32); accumulation is always fp32.
+ *   - Device pointers must be 16-byte aligned (NSA_ERR_ALIGN otherwise).
+ *   - Every check happens before the first enqueue: an error status means
+ *     nothing was launched.  NSA_ERR_LAUNCH reports a failed kernel launch;
+ *     work enqueued before it may have run.
+ *   - Calls on different streams may overlap only if each has its own
+ *     workspace and outputs.
+ *
+ * GPU support envelope: head_dim in {64, 128} for bf16, 64 for fp32; block
+ * 64; seq_len a multiple of 64 (at most 65536); Hq/Hkv in {1, 2, 4, 8, 16};
+ * 2 <= top_k <= 32; window >= 1.  Anything else returns NSA_ERR_UNSUPPORTED.
+ */
+#ifndef NSA_MI355X_H
+#define NSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NSA_ABI_VERSION 1
+
+typedef enum {
+  NSA_OK = 0,
+  NSA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  NSA_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes              */
+  NSA_ERR_DTYPE = -3,       /* unknown dtype                                   */
+  NSA_ERR_UNSUPPORTED = -4, /* valid NSA problem outside the GPU envelope      */
+  NSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required         */
+  NSA_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned         */
+  NSA_ERR_LAUNCH = -7       /* hipGetLastError reported a failed launch        */
+} nsa_status_t;
+
+typedef enum { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype_t;
+
+enum {
+  /* The compression branch is left out of `out` (as if g_cmp = 0); it is
+   * still computed because selection needs its scores. */
+  NSA_SKIP_CMP_OUT = 1,
+  /* The selection branch is left out of `out` (as if g_sel = 0); with
+   * NSA_SKIP_CMP_OUT as well, compression and selection are not computed at
+   * all (sliding-window-only, the pruned-branch layer of [SIC] Key claims). */
+  NSA_SKIP_SEL = 2,
+  /* The window branch is left out of `out` (as if g_win = 0). */
+  NSA_SKIP_WIN = 4,
+  /* `indices` is an INPUT: the given table (same layout and rules as the
+   * one the library writes) replaces the top-k step. */
+  NSA_INDICES_IN = 8
+};
+
+typedef struct {
+  int32_t batch;      /* B >= 1                                              */
+  int32_t seq_len;    /* T >= 1                                              */
+  int32_t n_q_heads;  /* Hq, a multiple of Hkv                               */
+  int32_t n_kv_heads; /* Hkv >= 1                                            */
+  int32_t head_dim;   /* D                                                   */
+  int32_t block;      /* compression block = selection block; 64 on the GPU  */
+  int32_t top_k;      /* selected blocks per (t, g) INCLUDING block 0 and
+                         the own block                                       */
+  int32_t window;     /* W: keys t-W < s <= t                                */
+  float scale;        /* tau; <= 0 selects 1/sqrt(head_dim)                   */
+  int32_t dtype;      /* nsa_dtype_t                                          */
+  uint32_t flags;     /* NSA_SKIP_* | NSA_INDICES_IN                          */
+} nsa_params_t;
+
+/* Version of this ABI (NSA_ABI_VERSION). */
+int nsa_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nsa_status_string(nsa_status_t status);
+
+/* Checks params against the rules above without touching any device.
+ * Returns NSA_OK, NSA_ERR_SHAPE, NSA_ERR_DTYPE or NSA_ERR_UNSUPPORTED. */
+nsa_status_t nsa_check_params(const nsa_params_t* p);
+
+/* Bytes of device workspace needed by nsa_forward (for_backward = 0) or by
+ * nsa_select_bwd (for_backward = 1).  Returns 0 for invalid params.  The size
+ * is monotone in seq_len and batch. */
+size_t nsa_workspace_size(const nsa_params_t* p, int for_backward);
+
+/* Compression step alone ([DSA] COMPRESSION; [SIC] Method: mean-pool over
+ * non-overlapping 64-token blocks).  Writes k_cmp and v_cmp
+ * [B][T/64][Hkv][D] in params->dtype: the fp32 mean rounded once (RNE for
+ * bf16).  No workspace. */
+nsa_status_t nsa_pool(const void* k, const void* v, const nsa_params_t* p,
+                      void* k_cmp, void* v_cmp, void* stream);
+
+/* Compression, compressed attention, block importance and top-k selection
+ * ([DSA] COMPRESSION and SELECTION; [SIC] Method and Key claims).
+ *   o_cmp   : [B][T][Hq][D], the UNGATED compressed-branch output, in
+ *             params->dtype (0 for t < 63).  Required.
+ *   indices : int32 [B][Hkv][T][top_k] selected blocks.  Required; ignored
+ *             flags: all.
+ * workspace: at least nsa_workspace_size(p, 0) bytes. */
+nsa_status_t nsa_compress_select(const void* q, const void* k, const void* v,
+                                 const nsa_params_t* p, void* o_cmp, int32_t* indices,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Full NSA forward (all three branches and the gated combination).
+ *   out      : required, [B][T][Hq][D] in params->dtype.
+ *   indices  : nullable output (or required input with NSA_INDICES_IN).
+ *   lse_sel  : nullable output, selection-branch log-sum-exp (for the
+ *              backward).
+ *   o_sel    : nullable output, ungated selection-branch output in
+ *              params->dtype (for the backward).
+ * workspace: at least nsa_workspace_size(p, 0) bytes. */
+nsa_status_t nsa_forward(const void* q, const void* k, const void* v, const void* gates,
+                         const nsa_params_t* p, void* out, int32_t* indices, float* lse_sel,
+                         void* o_sel, void* workspace, size_t ws_bytes, void* stream);
+
+/* nsa_forward, plus stage timing for measurement: `events` points to four
+ * caller-created hipEvent_t handles (passed as void*; any may be NULL), which
+ * are recorded on `stream` before the compression kernel, after it, after the
+ * compressed-attention/top-k kernel and after the selection/window/combine
+ * kernel.  Otherwise identical to nsa_forward (same checks, same results). */
+nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, const void* gates,
+                                 const nsa_params_t* p, void* out, int32_t* indices,
+                                 float* lse_sel, void* o_sel, void* workspace, size_t ws_bytes,
+                                 void* stream, void* const* events);
+
+/* Gradient of the selection branch with the selection and the gates held
+ * fixed ([SIC] Method: two-pass backward -- a query-stationary pass for dq and
+ * a key/value-stationary pass for dk/dv over the reverse block->query map;
+ * no atomics, so the result is bitwise reproducible).
+ *   dout            : gradient of `out`; the branch receives g_sel * dout.
+ *   indices, lse_sel, o_sel : as written by nsa_forward for the same inputs.
+ *   dq [B][T][Hq][D], dk, dv [B][T][Hkv][D] : outputs, overwritten.
+ * workspace: at least nsa_workspace_size(p, 1) bytes. */
+nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const void* gates,
+                            const int32_t* indices, const float* lse_sel, const void* o_sel,
+                            const void* dout, const nsa_params_t* p, void* dq, void* dk,
+                            void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_MI355X_H */

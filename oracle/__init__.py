@@ -66,7 +66,7 @@ def _load():
         lib.nsa_oracle_pool.argtypes = [ci, ci, ci, ci, ci, dp, dp]
         lib.nsa_oracle_pool.restype = ci
         lib.nsa_oracle_forward.argtypes = (
-            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [dp] * 5 + [ip, ci, dp, dp, ci]
+            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [dp] * 5 + [ip, ci, dp, dp, ip, ci, ci]
         )
         lib.nsa_oracle_forward.restype = ci
         lib.nsa_oracle_select_bwd.argtypes = (
@@ -104,13 +104,14 @@ def pool(x, blk: int = 64):
 
 
 def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: float | None = None,
-            indices=None, want_scores: bool = False, threads: int | None = None):
+            indices=None, want_scores: bool = False, rows=None, threads: int | None = None):
     """Full NSA forward.  Returns a dict of float64/int32 numpy arrays:
     out, o_cmp, o_sel, o_win [B,T,Hq,D]; lse_sel [B,Hq,T]; indices [B,Hkv,T,top_k];
     gap [B,Hkv,T]; scores [B,Hkv,T,nblk] (when want_scores).
 
     ``indices`` (optional, int32) freezes the selection to a table the oracle
-    produced earlier instead of running the top-k step."""
+    produced earlier instead of running the top-k step.  ``rows`` (optional)
+    restricts the computation to those query positions; other rows stay 0."""
     q, k, v, gates = _f64(q), _f64(k), _f64(v), _f64(gates)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -132,12 +133,15 @@ def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: fl
         idx = np.zeros((B, Hkv, T, top_k), dtype=np.int32)
     res["indices"] = idx
     scores = np.zeros((B, Hkv, T, nblk)) if want_scores else None
+    rows_a = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     rc = _load().nsa_oracle_forward(
         B, T, Hq, Hkv, D, blk, top_k, window, float(scale),
         _dptr(q), _dptr(k), _dptr(v), _dptr(gates),
         _dptr(res["out"]), _dptr(res["o_cmp"]), _dptr(res["o_sel"]), _dptr(res["o_win"]),
         _dptr(res["lse_sel"]), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
         1 if indices is not None else 0, _dptr(scores), _dptr(res["gap"]),
+        rows_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if rows_a is not None
+        else ctypes.POINTER(ctypes.c_int32)(), 0 if rows_a is None else len(rows_a),
         threads if threads is not None else default_threads())
     if rc != 0:
         raise ValueError(f"nsa_oracle_forward failed: {rc}")

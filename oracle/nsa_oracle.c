@@ -151,12 +151,16 @@ static int select_blocks(const oparams* p, int t, const double* S, int* out, dou
 
 /* ---- Full forward ---------------------------------------------------------
  * indices: if indices_in != 0 the given table is used instead of Step 4
- * (the oracle's own earlier table, e.g. to freeze the selection). */
+ * (the oracle's own earlier table, e.g. to freeze the selection).
+ * rows/nrows: if rows != NULL only those query positions are computed (the
+ * pooled blocks are still built from the whole sequence); other rows of the
+ * outputs are left untouched. */
 int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k, int window,
                        double scale, const double* q, const double* k, const double* v,
                        const double* gates, double* out, double* o_cmp, double* o_sel,
                        double* o_win, double* lse_sel, int32_t* indices, int indices_in,
-                       double* scores, double* gap, int nthreads) {
+                       double* scores, double* gap, const int32_t* rows, int nrows,
+                       int nthreads) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || blk < 1 || Hq % Hkv) return -2;
   if (top_k < 2 || window < 1) return -2;
   oparams p = {B, T, Hq, Hkv, D, blk, top_k, window, scale};
@@ -190,10 +194,14 @@ int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k,
 #pragma omp atomic write
       err = 1;
     } else {
+      /* rows (optional): only these query positions are computed. */
+      int nt = rows ? nrows : T;
 #pragma omp for schedule(dynamic, 16) collapse(2)
       for (int b = 0; b < B; ++b)
-        for (int t = 0; t < T; ++t)
+        for (int ti = 0; ti < nt; ++ti)
           for (int g = 0; g < Hkv; ++g) {
+            int t = rows ? rows[ti] : ti;
+            if (t < 0 || t >= T) continue;
             int ncv = (t + 1) / blk; /* complete blocks visible to t (reading) */
             /* Step 2: compressed attention per head; Step 3: importance.   */
             for (int j = 0; j <= nblk; ++j) S[j] = 0.0;

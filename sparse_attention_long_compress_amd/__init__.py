@@ -1,0 +1,215 @@
+"""MI355X (gfx950) Native Sparse Attention: thin Python binding of libnsa.so.
+
+Every function here only marshals arguments (torch device tensors -> raw
+pointers, sizes, the current HIP stream) and calls the C ABI declared in
+``include/nsa.h``; all computation runs in the library's HIP kernels.  PyTorch
+provides device memory and streams only.  If the library is not built, every
+call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnsa.so")
+
+NSA_BF16, NSA_FP32 = 0, 1
+SKIP_CMP_OUT, SKIP_SEL, SKIP_WIN, INDICES_IN = 1, 2, 4, 8
+
+EXPORTED = (
+    "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_workspace_size",
+    "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
+)
+
+
+class NsaError(RuntimeError):
+    pass
+
+
+class NsaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libnsa.so (raises NsaError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NsaError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_attention_long_compress_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(NsaParams)
+        vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        L.nsa_abi_version.restype = ctypes.c_int
+        L.nsa_status_string.argtypes = [ctypes.c_int]
+        L.nsa_status_string.restype = ctypes.c_char_p
+        L.nsa_check_params.argtypes = [P]
+        L.nsa_check_params.restype = ctypes.c_int
+        L.nsa_workspace_size.argtypes = [P, ctypes.c_int]
+        L.nsa_workspace_size.restype = ctypes.c_size_t
+        L.nsa_pool.argtypes = [vp, vp, P, vp, vp, vp]
+        L.nsa_pool.restype = ctypes.c_int
+        L.nsa_compress_select.argtypes = [vp, vp, vp, P, vp, i32p, vp, ctypes.c_size_t, vp]
+        L.nsa_compress_select.restype = ctypes.c_int
+        L.nsa_forward.argtypes = [vp, vp, vp, vp, P, vp, i32p, f32p, vp, vp, ctypes.c_size_t, vp]
+        L.nsa_forward.restype = ctypes.c_int
+        L.nsa_forward_profile.argtypes = [vp, vp, vp, vp, P, vp, i32p, f32p, vp, vp,
+                                          ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_void_p)]
+        L.nsa_forward_profile.restype = ctypes.c_int
+        L.nsa_select_bwd.argtypes = [vp, vp, vp, vp, i32p, f32p, vp, vp, P, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+        L.nsa_select_bwd.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().nsa_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise NsaError(f"{what}: {status_string(code)} ({code})")
+
+
+def make_params(B, T, Hq, Hkv, D, *, top_k, window, dtype, scale=None, flags=0, block=64):
+    return NsaParams(B, T, Hq, Hkv, D, block, top_k, window,
+                     float(scale) if scale else 0.0, dtype, flags)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return NSA_BF16
+    if t.dtype == torch.float32:
+        return NSA_FP32
+    raise NsaError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise NsaError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def params_for(q, k, *, top_k, window, scale=None, flags=0):
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return make_params(B, T, Hq, Hkv, D, top_k=top_k, window=window, dtype=_dtype_code(q),
+                       scale=scale, flags=flags)
+
+
+def workspace_size(p: NsaParams, backward: bool = False) -> int:
+    return int(lib().nsa_workspace_size(ctypes.byref(p), 1 if backward else 0))
+
+
+def alloc_workspace(p: NsaParams, device, backward: bool = False):
+    torch = _torch()
+    n = workspace_size(p, backward)
+    if n == 0:
+        _check(lib().nsa_check_params(ctypes.byref(p)), "nsa_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pool(k, v, *, stream=None):
+    """Mean-pooled keys/values [B, T/64, Hkv, D] (nsa_pool)."""
+    torch = _torch()
+    B, T, Hkv, D = k.shape
+    p = make_params(B, T, Hkv, Hkv, D, top_k=2, window=1, dtype=_dtype_code(k))
+    kc = torch.empty((B, T // 64, Hkv, D), dtype=k.dtype, device=k.device)
+    vc = torch.empty_like(kc)
+    _check(lib().nsa_pool(_ptr(k), _ptr(v), ctypes.byref(p), _ptr(kc), _ptr(vc), _stream(stream)),
+           "nsa_pool")
+    return kc, vc
+
+
+def compress_select(q, k, v, *, top_k, scale=None, workspace=None, stream=None):
+    """(o_cmp [B,T,Hq,D], indices [B,Hkv,T,top_k]) from nsa_compress_select."""
+    torch = _torch()
+    p = params_for(q, k, top_k=top_k, window=1, scale=scale)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device)
+    o_cmp = torch.empty_like(q)
+    idx = torch.empty((q.shape[0], k.shape[2], q.shape[1], top_k), dtype=torch.int32,
+                      device=q.device)
+    _check(lib().nsa_compress_select(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(o_cmp),
+                                     _ptr(idx), _ptr(ws), ws.numel(), _stream(stream)),
+           "nsa_compress_select")
+    return o_cmp, idx
+
+
+def forward(q, k, v, gates, *, top_k, window, scale=None, flags=0, indices=None,
+            want_indices=False, want_lse=False, want_o_sel=False, out=None, workspace=None,
+            stream=None, events=None):
+    """NSA forward (nsa_forward).  Returns a dict with 'out' and, when asked for,
+    'indices', 'lse_sel', 'o_sel'.  With ``indices`` given, the INDICES_IN flag
+    is set and that table replaces the top-k step.  ``events``: four raw
+    hipEvent_t handles (ints or None) recorded around the three kernels
+    (nsa_forward_profile)."""
+    torch = _torch()
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if indices is not None:
+        flags |= INDICES_IN
+    p = params_for(q, k, top_k=top_k, window=window, scale=scale, flags=flags)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device)
+    res = {"out": out if out is not None else torch.empty_like(q)}
+    idx = indices
+    if idx is None and want_indices:
+        idx = torch.empty((B, Hkv, T, top_k), dtype=torch.int32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if want_lse else None
+    o_sel = torch.empty_like(q) if want_o_sel else None
+    if events is None:
+        _check(lib().nsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), ctypes.byref(p),
+                                 _ptr(res["out"]), _ptr(idx), _ptr(lse), _ptr(o_sel), _ptr(ws),
+                                 ws.numel(), _stream(stream)), "nsa_forward")
+    else:
+        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+        _check(lib().nsa_forward_profile(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), ctypes.byref(p),
+                                         _ptr(res["out"]), _ptr(idx), _ptr(lse), _ptr(o_sel),
+                                         _ptr(ws), ws.numel(), _stream(stream), ev),
+               "nsa_forward_profile")
+    if idx is not None:
+        res["indices"] = idx
+    if lse is not None:
+        res["lse_sel"] = lse
+    if o_sel is not None:
+        res["o_sel"] = o_sel
+    return res
+
+
+def select_bwd(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, scale=None,
+               workspace=None, stream=None):
+    """(dq, dk, dv) of the selection branch (nsa_select_bwd)."""
+    torch = _torch()
+    p = params_for(q, k, top_k=top_k, window=1, scale=scale)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device, backward=True)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    _check(lib().nsa_select_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(indices),
+                                _ptr(lse_sel), _ptr(o_sel), _ptr(dout), ctypes.byref(p), _ptr(dq),
+                                _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
+           "nsa_select_bwd")
+    return dq, dk, dv

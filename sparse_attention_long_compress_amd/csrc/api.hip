@@ -1,0 +1,257 @@
+// api.hip -- the C ABI declared in include/nsa.h: parameter checks, workspace
+// carving and launch sequencing.  Nothing here computes; every step of the
+// path runs in the gfx950 kernels (pool.hip, cmp_select.hip, sel_win.hip,
+// bwd.hip).  No allocation, no synchronisation, no global mutable state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/nsa.h"
+#include "nsa_launch.h"
+
+using nsa::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+nsa_status_t check(const nsa_params_t* p) {
+  if (!p) return NSA_ERR_NULL;
+  if (p->batch < 1 || p->seq_len < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 ||
+      p->head_dim < 1 || p->block < 1 || p->top_k < 2 || p->window < 1)
+    return NSA_ERR_SHAPE;
+  if (p->n_q_heads % p->n_kv_heads != 0) return NSA_ERR_SHAPE;
+  if (p->dtype != NSA_BF16 && p->dtype != NSA_FP32) return NSA_ERR_DTYPE;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (p->head_dim != 64 && p->head_dim != 128) return NSA_ERR_UNSUPPORTED;
+  if (p->dtype == NSA_FP32 && p->head_dim != 64) return NSA_ERR_UNSUPPORTED;
+  if (p->block != 64) return NSA_ERR_UNSUPPORTED;
+  if (p->seq_len % 64 != 0 || p->seq_len > 65536) return NSA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return NSA_ERR_UNSUPPORTED;
+  if (p->top_k > 32) return NSA_ERR_UNSUPPORTED;
+  if (p->flags & ~0xFu) return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+Shape make_shape(const nsa_params_t* p) {
+  Shape s;
+  s.B = p->batch;
+  s.T = p->seq_len;
+  s.Hq = p->n_q_heads;
+  s.Hkv = p->n_kv_heads;
+  s.D = p->head_dim;
+  s.G = s.Hq / s.Hkv;
+  s.topk = p->top_k;
+  s.W = p->window;
+  s.nc = s.T / 64;
+  s.ncp = (s.nc + 31) / 32 * 32;
+  s.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  s.flags = p->flags;
+  return s;
+}
+
+// Forward workspace regions (byte offsets from the workspace base).
+struct FwdLayout {
+  size_t kc, kcl, vc, vct, vt, radius, o_cmp, ubound, indices, total;
+};
+FwdLayout fwd_layout(const Shape& s, size_t es) {
+  FwdLayout L;
+  size_t o = 0;
+  L.kc = o;      o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
+  L.kcl = o;     o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
+  L.vc = o;      o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
+  L.vct = o;     o += up((size_t)s.B * s.Hkv * s.D * s.ncp * es, kAlign);
+  L.vt = o;      o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
+  L.radius = o;  o += up((size_t)s.B * s.Hkv * s.ncp * 4, kAlign);
+  L.o_cmp = o;   o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
+  L.ubound = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
+  L.indices = o; o += up((size_t)s.B * s.Hkv * s.T * s.topk * 4, kAlign);
+  L.total = o;
+  return L;
+}
+
+// Backward workspace regions.
+struct BwdLayout {
+  size_t kt, vt, delta, dos, revmap, part, total;
+};
+BwdLayout bwd_layout(const Shape& s, size_t es) {
+  BwdLayout L;
+  size_t o = 0;
+  const size_t nblk = s.T / 64;
+  L.kt = o;     o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
+  L.vt = o;     o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
+  L.delta = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
+  L.dos = o;    o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
+  L.revmap = o; o += up((size_t)s.B * s.Hkv * nblk * nblk * 8, kAlign);
+  L.part = o;   o += up((size_t)s.B * s.Hkv * 2 * 64 * s.D * 4 * nblk, kAlign);
+  L.total = o;
+  return L;
+}
+
+inline size_t esize(const nsa_params_t* p) { return p->dtype == NSA_BF16 ? 2 : 4; }
+
+nsa_status_t launched(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int nsa_abi_version(void) { return NSA_ABI_VERSION; }
+
+const char* nsa_status_string(nsa_status_t st) {
+  switch (st) {
+    case NSA_OK: return "NSA_OK";
+    case NSA_ERR_NULL: return "NSA_ERR_NULL: a required pointer is NULL";
+    case NSA_ERR_SHAPE: return "NSA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case NSA_ERR_DTYPE: return "NSA_ERR_DTYPE: unknown dtype";
+    case NSA_ERR_UNSUPPORTED: return "NSA_ERR_UNSUPPORTED: outside the GPU support envelope";
+    case NSA_ERR_WORKSPACE: return "NSA_ERR_WORKSPACE: workspace missing or too small";
+    case NSA_ERR_ALIGN: return "NSA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case NSA_ERR_LAUNCH: return "NSA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "NSA_ERR_UNKNOWN";
+}
+
+nsa_status_t nsa_check_params(const nsa_params_t* p) { return check(p); }
+
+size_t nsa_workspace_size(const nsa_params_t* p, int for_backward) {
+  if (check(p) != NSA_OK) return 0;
+  const Shape s = make_shape(p);
+  return for_backward ? bwd_layout(s, esize(p)).total : fwd_layout(s, esize(p)).total;
+}
+
+nsa_status_t nsa_pool(const void* k, const void* v, const nsa_params_t* p, void* k_cmp,
+                      void* v_cmp, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!k || !v || !k_cmp || !v_cmp) return NSA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp)) return NSA_ERR_ALIGN;
+  const Shape s = make_shape(p);
+  return launched(nsa::launch_pool(p->dtype == NSA_BF16, s, k, v, k_cmp, v_cmp, nullptr, nullptr,
+                                   nullptr, nullptr, (hipStream_t)stream));
+}
+
+nsa_status_t nsa_compress_select(const void* q, const void* k, const void* v,
+                                 const nsa_params_t* p, void* o_cmp, int32_t* indices,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !o_cmp || !indices) return NSA_ERR_NULL;
+  if (!workspace) return NSA_ERR_WORKSPACE;
+  const Shape s = make_shape(p);
+  const size_t es = esize(p);
+  const FwdLayout L = fwd_layout(s, es);
+  if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_cmp) || !aligned16(indices) ||
+      ((uintptr_t)workspace % kAlign) != 0)
+    return NSA_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  const bool bf = p->dtype == NSA_BF16;
+  hipStream_t hs = (hipStream_t)stream;
+  void* kcl = bf ? ws + L.kcl : nullptr;
+  hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, nullptr,
+                                  (float*)(ws + L.radius), kcl, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, (const float*)(ws + L.radius),
+                             o_cmp, nullptr, indices, true, hs);
+  return launched(e);
+}
+
+nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, const void* gates,
+                                 const nsa_params_t* p, void* out, int32_t* indices,
+                                 float* lse_sel, void* o_sel, void* workspace, size_t ws_bytes,
+                                 void* stream, void* const* events) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !gates || !out) return NSA_ERR_NULL;
+  const bool idx_in = (p->flags & NSA_INDICES_IN) != 0;
+  if (idx_in && !indices) return NSA_ERR_NULL;
+  if (!workspace) return NSA_ERR_WORKSPACE;
+  const Shape s = make_shape(p);
+  const size_t es = esize(p);
+  const FwdLayout L = fwd_layout(s, es);
+  if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(out) ||
+      (indices && !aligned16(indices)) || (lse_sel && !aligned16(lse_sel)) ||
+      (o_sel && !aligned16(o_sel)) || ((uintptr_t)workspace % kAlign) != 0)
+    return NSA_ERR_ALIGN;
+
+  char* ws = (char*)workspace;
+  const bool bf = p->dtype == NSA_BF16;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool cmp_out = !(p->flags & NSA_SKIP_CMP_OUT);
+  const bool sel_out = !(p->flags & NSA_SKIP_SEL);
+  const bool need_sel = sel_out || lse_sel || o_sel;
+  const bool need_topk = !idx_in && (need_sel || indices);
+  const bool need_k2 = cmp_out || need_sel || need_topk;
+  int32_t* idx = indices ? indices : (int32_t*)(ws + L.indices);
+
+  void* kcl = bf ? ws + L.kcl : nullptr;
+  auto mark = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], hs);
+  };
+  mark(0);
+  hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, ws + L.vt,
+                                  (float*)(ws + L.radius), kcl, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  mark(1);
+  if (need_k2) {
+    e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, (const float*)(ws + L.radius),
+                               cmp_out ? ws + L.o_cmp : nullptr,
+                               need_sel ? (float*)(ws + L.ubound) : nullptr, idx, need_topk, hs);
+    if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  }
+  mark(2);
+  e = nsa::launch_sel_win(bf, s, q, k, ws + L.vt, gates, ws + L.o_cmp,
+                          (const float*)(ws + L.ubound), idx, out, lse_sel, o_sel, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  mark(3);
+  return NSA_OK;
+}
+
+nsa_status_t nsa_forward(const void* q, const void* k, const void* v, const void* gates,
+                         const nsa_params_t* p, void* out, int32_t* indices, float* lse_sel,
+                         void* o_sel, void* workspace, size_t ws_bytes, void* stream) {
+  return nsa_forward_profile(q, k, v, gates, p, out, indices, lse_sel, o_sel, workspace, ws_bytes,
+                             stream, nullptr);
+}
+
+nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const void* gates,
+                            const int32_t* indices, const float* lse_sel, const void* o_sel,
+                            const void* dout, const nsa_params_t* p, void* dq, void* dk,
+                            void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !gates || !indices || !lse_sel || !o_sel || !dout || !dq || !dk || !dv)
+    return NSA_ERR_NULL;
+  if (!workspace) return NSA_ERR_WORKSPACE;
+  const Shape s = make_shape(p);
+  const size_t es = esize(p);
+  const BwdLayout L = bwd_layout(s, es);
+  if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(indices) ||
+      !aligned16(lse_sel) || !aligned16(o_sel) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)workspace % kAlign) != 0)
+    return NSA_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  const bool bf = p->dtype == NSA_BF16;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e =
+      nsa::launch_pool(bf, s, k, v, nullptr, nullptr, nullptr, ws + L.vt, nullptr, nullptr, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_prep(bf, s, k, gates, o_sel, dout, ws + L.kt, (float*)(ws + L.delta),
+                           ws + L.dos, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_revmap(s, indices, (uint64_t*)(ws + L.revmap), hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_dq(bf, s, q, k, ws + L.kt, ws + L.vt, indices, lse_sel,
+                         (const float*)(ws + L.delta), ws + L.dos, dq, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_dkdv(bf, s, q, k, v, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
+                           (const uint64_t*)(ws + L.revmap), dk, dv, (float*)(ws + L.part), hs);
+  return launched(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// nsa_device.h -- device-side building blocks shared by the gfx950 kernels:
+// 16x16 MFMA fragments (bf16 and fp32 element types), cross-lane reductions,
+// conversions and small load/store helpers.
+//
+// Fragment conventions (one wavefront = 64 lanes, lane l, a = l / 16):
+//   A fragment of a 16 x 32 tile A[m][k] : lane l holds A[l % 16][8a + e], e = 0..7
+//   B fragment of a 32 x 16 tile B[k][n] : lane l holds B[8a + e][l % 16]
+//   C tile 16 x 16, fp32                 : lane l holds C[4a + r][l % 16], r = 0..3
+// The hardware pairs A and B elements by (lane / 16, element), so the product
+// is exact whatever physical k order the instruction uses.  bf16 fragments
+// feed one v_mfma_f32_16x16x32_bf16; fp32 fragments feed eight
+// v_mfma_f32_16x16x4_f32 (instruction e contracts the logical k = 8a + e).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+
+constexpr int kBlock = 64;  // compression block = selection block
+constexpr int kWave = 64;
+
+// Element-type traits: the fragment type holding 8 consecutive k elements.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+  typedef bf16x8 type;
+  static __device__ __forceinline__ type load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  static __device__ __forceinline__ type zero() {
+    type z;
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+  }
+  static __device__ __forceinline__ type from_f32(const float* x) {
+    type r;
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+    return r;
+  }
+};
+template <> struct Frag<float> {
+  typedef f32x8 type;
+  static __device__ __forceinline__ type load(const float* p) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = q[0], b = q[1];
+    type r;
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+  }
+  static __device__ __forceinline__ type zero() {
+    type z;
+    for (int i = 0; i < 8; ++i) z[i] = 0.0f;
+    return z;
+  }
+  static __device__ __forceinline__ type from_f32(const float* x) {
+    type r;
+    for (int i = 0; i < 8; ++i) r[i] = x[i];
+    return r;
+  }
+};
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, const bf16x8& a, const bf16x8& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Reductions across the four lane groups (a = l / 16) that share a column.
+__device__ __forceinline__ float colmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float colsum4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// DPP move inside 16-lane rows (ctrl is a DPP control code).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over aligned groups of G adjacent lanes inside each 16-lane row
+// (G in {1, 2, 4, 8, 16}); every lane of a group receives the group sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (G >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (G >= 8) v += dpp<0x141>(v);  // row_half_mirror: other quad of the 8
+  if constexpr (G >= 16) v += dpp<0x140>(v); // row_mirror: other half of the row
+  return v;
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+// Store 4 consecutive elements (fp32 values, converted to T).
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  bf16x4 r;
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  bf16x4 r = *reinterpret_cast<const bf16x4*>(p);
+  f32x4 o;
+  for (int i = 0; i < 4; ++i) o[i] = (float)r[i];
+  return o;
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace nsa

@@ -1,0 +1,54 @@
+// nsa_launch.h -- host-side launch functions of the gfx950 kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+// Shape of one call, resolved on the host.
+struct Shape {
+  int B, T, Hq, Hkv, D, G, topk, W;
+  int nc;      // complete compressed blocks = T / 64
+  int ncp;     // nc rounded up to a multiple of 32 (padded transposed copies)
+  float scale; // tau
+  uint32_t flags;
+};
+
+// K1: mean-pool.  kc/vc [B][nc][Hkv][D] (nullable); vct [B][Hkv][D][ncp]
+// (nullable); vt [B][Hkv][D][T] (nullable); radius [B][Hkv][ncp] fp32
+// (nullable); kc_lo [B][nc][Hkv][D] residual of the rounded kc (bf16 only,
+// nullable).
+hipError_t launch_pool(bool is_bf16, const Shape& s, const void* k, const void* v, void* kc,
+                       void* vc, void* vct, void* vt, float* radius, void* kc_lo,
+                       hipStream_t st);
+
+// K2: compressed attention + importance + top-k.
+//   o_cmp [B][T][Hq][D] (nullable), ubound [B][Hq][T] (nullable; log2 units),
+//   indices [B][Hkv][T][topk] (written unless do_topk == false).
+hipError_t launch_cmp_select(bool is_bf16, const Shape& s, const void* q, const void* kc,
+                             const void* kc_lo, const void* vct, const float* radius,
+                             void* o_cmp, float* ubound, int32_t* indices, bool do_topk,
+                             hipStream_t st);
+
+// K3: selection (forced + compacted free blocks) + window + gated combine.
+hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
+                          const void* vt, const void* gates, const void* o_cmp,
+                          const float* ubound, const int32_t* indices, void* out, float* lse,
+                          void* o_sel, hipStream_t st);
+
+// Backward (selection branch).
+hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* gates,
+                           const void* o_sel, const void* dout, void* kt, float* delta,
+                           void* dos, hipStream_t st);
+hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* revmap,
+                             hipStream_t st);
+hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* k,
+                         const void* kt, const void* vt, const int32_t* indices,
+                         const float* lse, const float* delta, const void* dos, void* dq,
+                         hipStream_t st);
+hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* k,
+                           const void* v, const float* lse, const float* delta, const void* dos,
+                           const uint64_t* revmap, void* dk, void* dv, float* part,
+                           hipStream_t st);
+
+}  // namespace nsa

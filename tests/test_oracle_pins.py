@@ -433,3 +433,16 @@ def test_select_bwd_central_finite_differences():
             fd = (loss(**{"qq": args_p["q"], "kk": args_p["k"], "vv": args_p["v"]})
                   - loss(**{"qq": args_m["q"], "kk": args_m["k"], "vv": args_m["v"]})) / (2 * h)
             assert abs(fd - grad[pos]) < 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_row_subset_matches_full_run():
+    # Restricting the oracle to some query positions changes nothing for them.
+    B, T, Hq, Hkv, D = 1, 700, 4, 2, 8
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=34)
+    full = oracle.forward(q, k, v, g, top_k=4, window=50)
+    rows = [0, 63, 64, 333, 699]
+    sub = oracle.forward(q, k, v, g, top_k=4, window=50, rows=rows)
+    for name in ("out", "o_cmp", "o_sel", "o_win"):
+        np.testing.assert_array_equal(sub[name][:, rows], full[name][:, rows])
+    np.testing.assert_array_equal(sub["indices"][:, :, rows], full["indices"][:, :, rows])
+    np.testing.assert_array_equal(sub["lse_sel"][:, :, rows], full["lse_sel"][:, :, rows])
