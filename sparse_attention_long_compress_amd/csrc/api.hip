@@ -46,7 +46,7 @@ Shape make_shape(const nsa_params_t* p) {
   s.topk = p->top_k;
   s.W = p->window;
   s.nc = s.T / 64;
-  s.ncp = (s.nc + 31) / 32 * 32;
+  s.ncp = (s.nc + 63) / 64 * 64;
   s.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   s.flags = p->flags;
   return s;
@@ -74,18 +74,19 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
 
 // Backward workspace regions.
 struct BwdLayout {
-  size_t kt, vt, delta, dos, revmap, part, total;
+  size_t kt, delta, dos, revmap, items, slots, part, total;
 };
 BwdLayout bwd_layout(const Shape& s, size_t es) {
   BwdLayout L;
   size_t o = 0;
   const size_t nblk = s.T / 64;
   L.kt = o;     o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
-  L.vt = o;     o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
   L.delta = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
   L.dos = o;    o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
   L.revmap = o; o += up((size_t)s.B * s.Hkv * nblk * nblk * 8, kAlign);
-  L.part = o;   o += up((size_t)s.B * s.Hkv * 2 * 64 * s.D * 4 * nblk, kAlign);
+  L.items = o;  o += up(nsa::bwd_items_bytes((int)nblk), kAlign);
+  L.slots = o;  o += up(nblk * 4, kAlign);
+  L.part = o;   o += up(nsa::bwd_part_floats(s) * 4, kAlign);
   L.total = o;
   return L;
 }
@@ -238,19 +239,17 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   char* ws = (char*)workspace;
   const bool bf = p->dtype == NSA_BF16;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e =
-      nsa::launch_pool(bf, s, k, v, nullptr, nullptr, nullptr, ws + L.vt, nullptr, nullptr, hs);
-  if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_prep(bf, s, k, gates, o_sel, dout, ws + L.kt, (float*)(ws + L.delta),
-                           ws + L.dos, hs);
+  hipError_t e = nsa::launch_bwd_prep(bf, s, k, gates, o_sel, dout, ws + L.kt,
+                                      (float*)(ws + L.delta), ws + L.dos, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_revmap(s, indices, (uint64_t*)(ws + L.revmap), hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_dq(bf, s, q, k, ws + L.kt, ws + L.vt, indices, lse_sel,
-                         (const float*)(ws + L.delta), ws + L.dos, dq, hs);
+  e = nsa::launch_bwd_dq(bf, s, q, k, ws + L.kt, v, indices, lse_sel, (const float*)(ws + L.delta),
+                         ws + L.dos, dq, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_dkdv(bf, s, q, k, v, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
-                           (const uint64_t*)(ws + L.revmap), dk, dv, (float*)(ws + L.part), hs);
+                           (const uint64_t*)(ws + L.revmap), dk, dv, ws + L.items,
+                           (int*)(ws + L.slots), (float*)(ws + L.part), hs);
   return launched(e);
 }
 

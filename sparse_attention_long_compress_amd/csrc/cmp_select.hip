@@ -12,16 +12,18 @@
 // One workgroup (4 waves) per (tile of P query positions, KV group g, batch b);
 // every position of a tile lies in the same 64-token block c, so they share the
 // candidate set 1..c-1.  Query rows are ordered (position, head), 16 rows form
-// one MFMA column group, each wave owns R/4 rows.
-//   Pass 1: S^T = Kc Q^T on bf16/fp32 MFMA, online softmax, o_cmp = P Vc, and
+// one MFMA column group, each wave owns R/4 rows.  Pooled keys and values are
+// staged in LDS 64 blocks at a time (shared by all waves).
+//   Pass 1: S^T = Kc Q^T on MFMA, online softmax, o_cmp = P Vc, and
 //           U = max_j (tau q.Kc_j + tau |q| radius_j) over blocks 0 .. own, an
 //           upper bound of every logit the row's selected blocks can produce
 //           (log2 units).
 //   Pass 2: recompute S^T, p = exp(s - lse), sum p over the G heads of each
 //           position with DPP (adjacent lanes), stage S[position][block] in LDS
-//           64 candidates at a time; one lane per position keeps its top-m
-//           list in registers.  Each candidate is a 32-bit key: the score in
-//           fixed point (21 bits over [0, G], resolution G / 2^21) above the
+//           64 candidates at a time; each wave scans a quarter of them with one
+//           lane per position keeping a top-m list in registers, and the four
+//           lists are merged at the end.  A candidate is a 32-bit key: the score
+//           in fixed point (21 bits over [0, G], resolution G / 2^21) above the
 //           field 2047 - j, so "higher score, then lower index" is one unsigned
 //           compare and inserting into the sorted list is one v_med3_u32 per
 //           entry.
@@ -45,24 +47,44 @@ __device__ __forceinline__ uint32_t topk_key(float score, float qscale, int j) {
 __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
 }
+template <int N>
+__device__ __forceinline__ void insert_desc(uint32_t (&list)[N], uint32_t x) {
+#pragma unroll
+  for (int i = N - 1; i >= 1; --i) list[i] = umed3(list[i], list[i - 1], x);
+  list[0] = max(list[0], x);
+}
+
+template <typename T, int D, int G>
+struct K2Cfg {
+  static constexpr int P = (256 / G) < 64 ? (256 / G) : 64;  // positions per tile
+  static constexpr int R = P * G;                            // rows per tile
+  static constexpr int RWV = R / 4;                          // rows per wave
+  static constexpr int CGW = RWV / 16;                       // column groups per wave
+  static constexpr int KS = D / 32, MT = D / 16;
+  static constexpr int KST = D + 8;   // LDS row stride of the pooled-key chunk
+  static constexpr int VST = 64 + 8;  // LDS row stride of the pooled-value chunk
+};
 
 template <typename T, int D, int G, int LMAX>
 __global__ __launch_bounds__(256) void cmp_select_kernel(
     Shape s, const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ kcl,
-    const T* __restrict__ vct,
-    const float* __restrict__ radius, T* __restrict__ o_cmp, float* __restrict__ ubound,
-    int32_t* __restrict__ indices, int do_topk) {
-  constexpr int P = (256 / G) < 64 ? (256 / G) : 64;  // positions per tile
-  constexpr int R = P * G;                            // rows per tile
-  constexpr int CGW = (R / 4) / 16 > 0 ? (R / 4) / 16 : 1;  // column groups per wave
-  constexpr int KS = D / 32;                          // k-steps over the head dim
-  constexpr int MT = D / 16;                          // 16-row tiles over the head dim
-  constexpr int CHK = 64;                             // candidates staged per round
+    const T* __restrict__ vct, const float* __restrict__ radius, T* __restrict__ o_cmp,
+    float* __restrict__ ubound, int32_t* __restrict__ indices, int do_topk) {
+  typedef K2Cfg<T, D, G> C;
+  constexpr int P = C::P, CGW = C::CGW, KS = C::KS, MT = C::MT, KST = C::KST, VST = C::VST;
   typedef typename Frag<T>::type FragT;
+  constexpr int EPV = 16 / sizeof(T);
 
-  __shared__ float S_l[P][CHK + 1];
+  __shared__ __align__(16) T Ks[64 * KST];
+  __shared__ __align__(16) T Ls[64 * KST];
+  __shared__ __align__(16) T Vs[D * VST];
+  __shared__ float S_l[P][65];
+  __shared__ uint32_t mlist[3][P][LMAX];
 
-  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int NTL = s.T / P;
+  int bg, tile;
+  xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
   const int t0 = tile * P;
   const int c = t0 / kBlock;  // own block of every position in the tile
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
@@ -71,100 +93,138 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
   const int nvis = min(s.nc, c + 1);  // compressed blocks any row of the tile may see
   const int m_free = s.topk - (c == 0 ? 1 : 2);
   const bool need_scores = do_topk && (c - 1 > m_free);
+  const bool has_lo = kcl != nullptr;
 
   const size_t kc_row = (size_t)s.Hkv * D;
   const T* kc_b = kc + (size_t)b * s.nc * kc_row + (size_t)g * D;
-  const T* kcl_b = kcl ? kcl + (size_t)b * s.nc * kc_row + (size_t)g * D : nullptr;
+  const T* kcl_b = has_lo ? kcl + (size_t)b * s.nc * kc_row + (size_t)g * D : nullptr;
   const T* vct_b = vct + ((size_t)b * s.Hkv + g) * (size_t)D * s.ncp;
   const float* rad_b = radius ? radius + ((size_t)b * s.Hkv + g) * s.ncp : nullptr;
 
-  float lse2[CGW];
+  // stage pooled keys (and the residual) of blocks jb .. jb+63, and optionally
+  // the pooled values; rows past the last complete block are clamped (masked)
+  auto stage = [&](int jb, bool with_v) {
+    for (int i = threadIdx.x; i < 64 * (D / EPV); i += 256) {
+      const int r = i / (D / EPV), c8 = i % (D / EPV);
+      const int key = min(jb + r, s.nc - 1);
+      *reinterpret_cast<int4*>(Ks + r * KST + c8 * EPV) =
+          *reinterpret_cast<const int4*>(kc_b + (size_t)key * kc_row + c8 * EPV);
+      if (has_lo)
+        *reinterpret_cast<int4*>(Ls + r * KST + c8 * EPV) =
+            *reinterpret_cast<const int4*>(kcl_b + (size_t)key * kc_row + c8 * EPV);
+    }
+    if (with_v)
+      for (int i = threadIdx.x; i < D * (64 / EPV); i += 256) {
+        const int r = i / (64 / EPV), c8 = i % (64 / EPV);
+        *reinterpret_cast<int4*>(Vs + r * VST + c8 * EPV) =
+            *reinterpret_cast<const int4*>(vct_b + (size_t)r * s.ncp + jb + c8 * EPV);
+      }
+  };
+  // S^T tile u of the 32-key half h of the staged chunk (keys h*32 + 8a + 4u + r)
+  auto scores = [&](int h, int u, const FragT (&qf)[KS]) -> f32x4 {
+    const int kr = h * 32 + 8 * (col / 4) + 4 * u + (col % 4);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mma(acc, Frag<T>::load(Ks + kr * KST + ks * 32 + a * 8), qf[ks]);
+    if (has_lo) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mma(acc, Frag<T>::load(Ls + kr * KST + ks * 32 + a * 8), qf[ks]);
+    }
+    return acc;
+  };
 
-  // ------------------------------------------------------------------ pass 1
+  // rows of this wave: (position, head) with lane column col in group cg
+  FragT qf[CGW][KS];
+  int tpos[CGW], hidx[CGW], ppos[CGW];
+  float qnorm[CGW];
+#pragma unroll
   for (int cg = 0; cg < CGW; ++cg) {
-    const int row = w * (R / 4) + cg * 16 + col;
-    const bool row_ok = row < R;
-    const int p = (row_ok ? row : 0) / G, hh = (row_ok ? row : 0) % G;
-    const int t = t0 + p, h = g * G + hh;
-    const T* qrow = q + (((size_t)b * s.T + t) * s.Hq + h) * D;
-    FragT qf[KS];
+    const int row = w * C::RWV + cg * 16 + col;
+    ppos[cg] = row / G;
+    tpos[cg] = t0 + ppos[cg];
+    hidx[cg] = g * G + row % G;
+    const T* qrow = q + (((size_t)b * s.T + tpos[cg]) * s.Hq + hidx[cg]) * D;
     float qn2 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = Frag<T>::load(qrow + ks * 32 + a * 8);
+      qf[cg][ks] = Frag<T>::load(qrow + ks * 32 + a * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qn2 += (float)qf[ks][e] * (float)qf[ks][e];
+      for (int e = 0; e < 8; ++e) qn2 += (float)qf[cg][ks][e] * (float)qf[cg][ks][e];
     }
-    const float qnorm = sqrtf(colsum4(qn2));
-    float m = -INFINITY, lsum = 0.f, ub = -INFINITY;
-    f32x4 o[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] = zero4();
+    qnorm[cg] = sqrtf(xsum4(qn2));
+  }
 
-    for (int j0 = 0; j0 < nvis; j0 += 32) {
-      f32x4 st[2];
+  // ------------------------------------------------------------------ pass 1
+  float m[CGW], lsum[CGW], ub[CGW], lse2[CGW];
+  f32x4 o[CGW][MT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int key = j0 + 8 * (col / 4) + 4 * u + (col % 4);
-        key = min(key, s.nc - 1);
-        const T* krow = kc_b + (size_t)key * kc_row;
-        f32x4 acc = zero4();
+  for (int cg = 0; cg < CGW; ++cg) {
+    m[cg] = -INFINITY;
+    lsum[cg] = 0.f;
+    ub[cg] = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mma(acc, Frag<T>::load(krow + ks * 32 + a * 8), qf[ks]);
-        if (kcl_b) {
-          const T* lrow = kcl_b + (size_t)key * kc_row;
+    for (int mt = 0; mt < MT; ++mt) o[cg][mt] = zero4();
+  }
+  for (int jb = 0; jb < nvis; jb += 64) {
+    __syncthreads();
+    stage(jb, true);
+    __syncthreads();
+    for (int h = 0; h < 2 && jb + h * 32 < nvis; ++h) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mma(acc, Frag<T>::load(lrow + ks * 32 + a * 8), qf[ks]);
+      for (int cg = 0; cg < CGW; ++cg) {
+        float x[8], pv[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 st = scores(h, u, qf[cg]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = jb + h * 32 + 8 * a + 4 * u + r;
+            const bool vis = (jj * kBlock + kBlock - 1 <= tpos[cg]) && jj < s.nc;
+            const float xv = st[r] * c1;
+            x[4 * u + r] = vis ? xv : -INFINITY;
+            // bound over every block the row may select: 0 .. own (complete or
+            // not, all keys of a block lie within its radius of its mean)
+            if (rad_b && jj <= c && jj < s.nc)
+              ub[cg] = fmaxf(ub[cg], xv + qnorm[cg] * c1 * rad_b[jj]);
+          }
         }
-        st[u] = acc;
-      }
-      float x[8], pv[8];
+        float mx = x[0];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+        mx = xmax4(mx);
+        const float mn = fmaxf(m[cg], mx);
+        float alpha = 1.f, psum = 0.f;
+        if (mn == -INFINITY) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jj = j0 + 8 * a + 4 * u + r;
-          const bool vis = row_ok && (jj * kBlock + kBlock - 1 <= t) && jj < s.nc;
-          const float xv = st[u][r] * c1;
-          x[4 * u + r] = vis ? xv : -INFINITY;
-          // bound over every block the row may select: 0 .. own (complete
-          // or not, the block's keys are all within radius of its mean)
-          if (row_ok && rad_b && jj <= c && jj < s.nc)
-            ub = fmaxf(ub, xv + qnorm * c1 * rad_b[jj]);
+          for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+        } else {
+          alpha = fast_exp2(m[cg] - mn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { pv[e] = fast_exp2(x[e] - mn); psum += pv[e]; }
         }
-      float mx = x[0];
+        lsum[cg] = lsum[cg] * alpha + xsum4(psum);
+        m[cg] = mn;
+        const FragT pf = Frag<T>::from_f32(pv);
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = colmax4(mx);
-      const float mn = fmaxf(m, mx);
-      float alpha = 1.f, psum = 0.f;
-      if (mn == -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-      } else {
-        alpha = fast_exp2(m - mn);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pv[e] = fast_exp2(x[e] - mn); psum += pv[e]; }
-      }
-      lsum = lsum * alpha + colsum4(psum);
-      m = mn;
-      const FragT pf = Frag<T>::from_f32(pv);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const FragT vf = Frag<T>::load(vct_b + (size_t)(mt * 16 + col) * s.ncp + j0 + 8 * a);
-        o[mt] = mma(o[mt] * alpha, vf, pf);
+        for (int mt = 0; mt < MT; ++mt)
+          o[cg][mt] = mma(o[cg][mt] * alpha,
+                          Frag<T>::load(Vs + (mt * 16 + col) * VST + h * 32 + 8 * a), pf);
       }
     }
-    lse2[cg] = (lsum > 0.f) ? m + __log2f(lsum) : -INFINITY;
-    if (o_cmp && row_ok) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      T* orow = o_cmp + (((size_t)b * s.T + t) * s.Hq + h) * D;
+  }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) store4(orow + mt * 16 + 4 * a, o[mt] * inv);
+  for (int cg = 0; cg < CGW; ++cg) {
+    lse2[cg] = (lsum[cg] > 0.f) ? m[cg] + __log2f(lsum[cg]) : -INFINITY;
+    if (o_cmp) {
+      const float inv = lsum[cg] > 0.f ? 1.f / lsum[cg] : 0.f;
+      T* orow = o_cmp + (((size_t)b * s.T + tpos[cg]) * s.Hq + hidx[cg]) * D;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) store4(orow + mt * 16 + 4 * a, o[cg][mt] * inv);
     }
-    if (ubound && row_ok) {
-      ub = colmax4(ub);
-      if (a == 0) ubound[((size_t)b * s.Hq + h) * s.T + t] = ub;
+    if (ubound) {
+      const float u2 = xmax4(ub[cg]);
+      if (a == 0) ubound[((size_t)b * s.Hq + hidx[cg]) * s.T + tpos[cg]] = u2;
     }
   }
 
@@ -174,60 +234,53 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
   uint32_t list[LMAX];
 #pragma unroll
   for (int i = 0; i < LMAX; ++i) list[i] = 0u;
+  const float qscale = 2097152.f / (float)G;
 
   if (need_scores) {
-    for (int jb = 1; jb <= c - 1; jb += CHK) {
-      for (int cg = 0; cg < CGW; ++cg) {
-        const int row = w * (R / 4) + cg * 16 + col;
-        const bool row_ok = row < R;
-        const int p = (row_ok ? row : 0) / G, hh = (row_ok ? row : 0) % G;
-        const int t = t0 + p, h = g * G + hh;
-        const T* qrow = q + (((size_t)b * s.T + t) * s.Hq + h) * D;
-        FragT qf[KS];
+    for (int jb = 1; jb <= c - 1; jb += 64) {
+      __syncthreads();
+      stage(jb, false);
+      __syncthreads();
+      for (int h = 0; h < 2 && jb + h * 32 <= c - 1; ++h) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = Frag<T>::load(qrow + ks * 32 + a * 8);
-        for (int j0 = jb; j0 < jb + CHK && j0 <= c - 1; j0 += 32) {
+        for (int cg = 0; cg < CGW; ++cg) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            int key = j0 + 8 * (col / 4) + 4 * u + (col % 4);
-            key = min(key, s.nc - 1);
-            const T* krow = kc_b + (size_t)key * kc_row;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mma(acc, Frag<T>::load(krow + ks * 32 + a * 8), qf[ks]);
-            if (kcl_b) {
-              const T* lrow = kcl_b + (size_t)key * kc_row;
-#pragma unroll
-              for (int ks = 0; ks < KS; ++ks)
-                acc = mma(acc, Frag<T>::load(lrow + ks * 32 + a * 8), qf[ks]);
-            }
+            const f32x4 st = scores(h, u, qf[cg]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int jj = j0 + 8 * a + 4 * u + r;
-              float pr = row_ok ? fast_exp2(acc[r] * c1 - lse2[cg]) : 0.f;
+              const int jj = jb + h * 32 + 8 * a + 4 * u + r;
+              float pr = fast_exp2(st[r] * c1 - lse2[cg]);
               pr = group_sum<G>(pr);
-              if (row_ok && (col % G) == 0 && jj <= c - 1) S_l[p][jj - jb] = pr;
+              if ((col % G) == 0 && jj <= c - 1) S_l[ppos[cg]][jj - jb] = pr;
             }
           }
         }
       }
       __syncthreads();
-      if (threadIdx.x < P) {
-        const int jend = min(jb + CHK, c);
-        const float qscale = 2097152.f / (float)G;
-        for (int jj = jb; jj < jend; ++jj) {
-          const uint32_t x = topk_key(S_l[threadIdx.x][jj - jb], qscale, jj);
-#pragma unroll
-          for (int i = LMAX - 1; i >= 1; --i) list[i] = umed3(list[i], list[i - 1], x);
-          list[0] = max(list[0], x);
-        }
+      // wave w scans candidates jb + 16w .. jb + 16w + 15, one lane per position
+      if (l < P) {
+        const int j0 = jb + 16 * w, j1 = min(jb + 16 * w + 16, c);
+        for (int jj = j0; jj < j1; ++jj) insert_desc(list, topk_key(S_l[l][jj - jb], qscale, jj));
       }
-      __syncthreads();
+    }
+    // merge the four per-wave lists into wave 0's
+    __syncthreads();
+    if (w > 0 && l < P) {
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) mlist[w - 1][l][i] = list[i];
+    }
+    __syncthreads();
+    if (w == 0 && l < P) {
+      // a rolled loop: fully unrolled chains of med3 insertions make the
+      // compiler's min/max combining blow up
+#pragma nounroll
+      for (int vi = 0; vi < 3 * LMAX; ++vi) insert_desc(list, mlist[vi / LMAX][l][vi % LMAX]);
     }
   }
 
-  if (threadIdx.x < P) {
-    const int t = t0 + threadIdx.x;
+  if (w == 0 && l < P) {
+    const int t = t0 + l;
     constexpr int KMAX = LMAX + 2;
     int sel[KMAX];
 #pragma unroll
@@ -259,8 +312,8 @@ template <typename T, int D, int G>
 static hipError_t launch_cs(const Shape& s, const void* q, const void* kc, const void* kcl,
                             const void* vct, const float* radius, void* o_cmp, float* ubound,
                             int32_t* indices, bool do_topk, hipStream_t st) {
-  constexpr int P = (256 / G) < 64 ? (256 / G) : 64;
-  dim3 grid(s.T / P, s.Hkv, s.B);
+  constexpr int P = K2Cfg<T, D, G>::P;
+  dim3 grid(s.T / P * s.Hkv * s.B);
   if (s.topk - 2 <= 16)
     hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 16>), grid, dim3(256), 0, st, s, (const T*)q,
                        (const T*)kc, (const T*)kcl, (const T*)vct, radius, (T*)o_cmp, ubound,

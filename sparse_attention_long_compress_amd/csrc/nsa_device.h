@@ -131,4 +131,44 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max / sum over the four lane groups (l / 16) that hold one MFMA column,
+// with the gfx950 lane-swap instructions (VALU; no LDS crossbar traffic)
+__device__ __forceinline__ float xmax4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Work order for a 1-D grid over (batch * kv-group) x tiles.  Workgroups are
+// dealt to the 8 XCDs round-robin (XCD = id % 8), each XCD with its own L2.
+// When the number of (batch, group) pairs NBG divides 8 or is a multiple of
+// it, every XCD is given whole (batch, group) pairs -- their K/V stay in that
+// XCD's L2 -- and within an XCD tiles go out largest-first (the tile cost
+// grows with its position), so the last wave of workgroups is short.
+__device__ __forceinline__ void xcd_order(int L, int N, int NBG, int NTL, int& bg, int& tile) {
+  constexpr int X = 8;
+  const int x = L % X, sl = L / X;
+  if (N % X == 0 && X % NBG == 0) {
+    const int share = X / NBG;  // XCDs per (batch, group)
+    bg = x / share;
+    const int r = sl * share + x % share;
+    tile = NTL - 1 - r;
+  } else if (N % X == 0 && NBG % X == 0) {
+    const int per = NBG / X;    // (batch, group) pairs per XCD
+    bg = x + X * (sl / NTL);
+    (void)per;
+    tile = NTL - 1 - sl % NTL;
+  } else {
+    bg = L / NTL;
+    tile = NTL - 1 - L % NTL;
+  }
+}
+
 }  // namespace nsa

@@ -9,7 +9,7 @@ namespace nsa {
 struct Shape {
   int B, T, Hq, Hkv, D, G, topk, W;
   int nc;      // complete compressed blocks = T / 64
-  int ncp;     // nc rounded up to a multiple of 32 (padded transposed copies)
+  int ncp;     // nc rounded up to a multiple of 64 (padded transposed copies)
   float scale; // tau
   uint32_t flags;
 };
@@ -43,12 +43,14 @@ hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const vo
 hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* revmap,
                              hipStream_t st);
 hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* k,
-                         const void* kt, const void* vt, const int32_t* indices,
+                         const void* kt, const void* v, const int32_t* indices,
                          const float* lse, const float* delta, const void* dos, void* dq,
                          hipStream_t st);
 hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* k,
                            const void* v, const float* lse, const float* delta, const void* dos,
-                           const uint64_t* revmap, void* dk, void* dv, float* part,
-                           hipStream_t st);
+                           const uint64_t* revmap, void* dk, void* dv, void* items_ws,
+                           int* slot_base, float* part, hipStream_t st);
+size_t bwd_items_bytes(int nblk);
+size_t bwd_part_floats(const Shape& s);
 
 }  // namespace nsa

@@ -56,7 +56,7 @@ template <typename T, int D, int G>
 struct K3Cfg {
   // waves per workgroup and target rows per wave: both accumulators (selection
   // and window, 2 * rows/16 * D/4 fp32 registers per lane) must fit in registers
-  static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+  static constexpr int NW = (sizeof(T) == 2 && D == 128) ? 8 : 4;
   static constexpr int NT = NW * 64;
   static constexpr int RWT = (sizeof(T) == 2 && D == 128) ? 32 : 64;
   static constexpr int P = (NW * RWT / G) < 128 ? (NW * RWT / G) : 128;  // positions per tile
@@ -87,20 +87,6 @@ template <typename T> struct V16;
 template <> struct V16<bf16> { typedef bf16x8 type; };
 template <> struct V16<float> { typedef f32x4 type; };
 
-// max / sum over the four lane groups that hold one MFMA column
-__device__ __forceinline__ float xmax4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float xsum4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <typename T, int D, int G>
 __global__ __launch_bounds__((K3Cfg<T, D, G>::NT)) void sel_win_kernel(Shape s, SelWinArgs args) {
   typedef K3Cfg<T, D, G> C;
@@ -114,7 +100,10 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT)) void sel_win_kernel(Shape s, 
   const T* __restrict__ k = (const T*)args.k;
   const T* __restrict__ vt = (const T*)args.vt;
 
-  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int NTL = (s.T + P - 1) / P;
+  int bg, tile;
+  xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
   const int t0 = tile * P;
   const int nvalid = min(P, s.T - t0);  // the last tile may be ragged (T % P != 0)
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
@@ -489,7 +478,7 @@ static hipError_t launch_sw(const Shape& s, const SelWinArgs& args, hipStream_t 
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((s.T + C::P - 1) / C::P, s.Hkv, s.B);
+  dim3 grid((s.T + C::P - 1) / C::P * s.Hkv * s.B);
   hipLaunchKernelGGL((sel_win_kernel<T, D, G>), grid, dim3(C::NT), lds, st, s, args);
   return hipGetLastError();
 }

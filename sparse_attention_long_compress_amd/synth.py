@@ -70,11 +70,16 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 
 def draw(wl: Workload, *, planted_sigma: float = 0.0, with_dout: bool = False,
-         seq_len: int | None = None):
+         seq_len: int | None = None, prefix: int | None = None):
     """Draw float32 numpy inputs for ``wl`` (optionally with a shorter sequence).
 
+    ``seq_len`` draws a different, shorter workload; ``prefix`` draws the full
+    workload and keeps its first ``prefix`` positions (a causal slice of it).
     Returns dict(q, k, v, gates[, dout]) of float32 arrays in the layouts
     q/dout [B,T,Hq,D], k/v [B,T,Hkv,D], gates [B,T,Hq,3]."""
+    if prefix is not None:
+        full = draw(wl, planted_sigma=planted_sigma, with_dout=with_dout)
+        return {k: np.ascontiguousarray(v[:, :prefix]) for k, v in full.items()}
     T = seq_len if seq_len is not None else wl.seq_len
     B, Hq, Hkv, D = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
     rng = np.random.default_rng(wl.seed)

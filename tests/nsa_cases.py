@@ -22,8 +22,10 @@ def tol(dtype: str):
     return (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
 
 
-def device_inputs(wl: Workload, *, seq_len=None, planted_sigma=0.0, with_dout=False, q_scale=1.0):
-    arrs = draw(wl, planted_sigma=planted_sigma, with_dout=with_dout, seq_len=seq_len)
+def device_inputs(wl: Workload, *, seq_len=None, planted_sigma=0.0, with_dout=False, q_scale=1.0,
+                  prefix=None):
+    arrs = draw(wl, planted_sigma=planted_sigma, with_dout=with_dout, seq_len=seq_len,
+                prefix=prefix)
     if q_scale != 1.0:
         arrs["q"] = arrs["q"] * np.float32(q_scale)
     cpu = to_dtype(arrs, wl.dtype)
