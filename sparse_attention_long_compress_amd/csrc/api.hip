@@ -54,7 +54,7 @@ Shape make_shape(const nsa_params_t* p) {
 
 // Forward workspace regions (byte offsets from the workspace base).
 struct FwdLayout {
-  size_t kc, kcl, vc, vct, vt, radius, o_cmp, ubound, indices, total;
+  size_t kc, kcl, vc, vct, kvimg, knorm, o_cmp, indices, total;
 };
 FwdLayout fwd_layout(const Shape& s, size_t es) {
   FwdLayout L;
@@ -63,10 +63,9 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
   L.kcl = o;     o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
   L.vc = o;      o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
   L.vct = o;     o += up((size_t)s.B * s.Hkv * s.D * s.ncp * es, kAlign);
-  L.vt = o;      o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
-  L.radius = o;  o += up((size_t)s.B * s.Hkv * s.ncp * 4, kAlign);
+  L.kvimg = o;   o += up((size_t)s.B * s.Hkv * s.nc * 2 * 64 * s.D * es, kAlign);
+  L.knorm = o;   o += up((size_t)s.B * s.Hkv * s.nc * 4, kAlign);
   L.o_cmp = o;   o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
-  L.ubound = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
   L.indices = o; o += up((size_t)s.B * s.Hkv * s.T * s.topk * 4, kAlign);
   L.total = o;
   return L;
@@ -153,10 +152,10 @@ nsa_status_t nsa_compress_select(const void* q, const void* k, const void* v,
   hipStream_t hs = (hipStream_t)stream;
   void* kcl = bf ? ws + L.kcl : nullptr;
   hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, nullptr,
-                                  (float*)(ws + L.radius), kcl, hs);
+                                  nullptr, kcl, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, (const float*)(ws + L.radius),
-                             o_cmp, nullptr, indices, true, hs);
+  e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, nullptr, o_cmp, nullptr,
+                             indices, true, hs);
   return launched(e);
 }
 
@@ -186,7 +185,7 @@ nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, co
   const bool sel_out = !(p->flags & NSA_SKIP_SEL);
   const bool need_sel = sel_out || lse_sel || o_sel;
   const bool need_topk = !idx_in && (need_sel || indices);
-  const bool need_k2 = cmp_out || need_sel || need_topk;
+  const bool need_k2 = cmp_out || need_topk;
   int32_t* idx = indices ? indices : (int32_t*)(ws + L.indices);
 
   void* kcl = bf ? ws + L.kcl : nullptr;
@@ -194,19 +193,18 @@ nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, co
     if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], hs);
   };
   mark(0);
-  hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, ws + L.vt,
-                                  (float*)(ws + L.radius), kcl, hs);
+  hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, ws + L.kvimg,
+                                  (float*)(ws + L.knorm), kcl, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   mark(1);
   if (need_k2) {
-    e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, (const float*)(ws + L.radius),
-                               cmp_out ? ws + L.o_cmp : nullptr,
-                               need_sel ? (float*)(ws + L.ubound) : nullptr, idx, need_topk, hs);
+    e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, nullptr,
+                               cmp_out ? ws + L.o_cmp : nullptr, nullptr, idx, need_topk, hs);
     if (e != hipSuccess) return NSA_ERR_LAUNCH;
   }
   mark(2);
-  e = nsa::launch_sel_win(bf, s, q, k, ws + L.vt, gates, ws + L.o_cmp,
-                          (const float*)(ws + L.ubound), idx, out, lse_sel, o_sel, hs);
+  e = nsa::launch_sel_win(bf, s, q, k, ws + L.kvimg, gates, ws + L.o_cmp,
+                          (const float*)(ws + L.knorm), idx, out, lse_sel, o_sel, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   mark(3);
   return NSA_OK;

@@ -146,6 +146,30 @@ __device__ __forceinline__ float xsum4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Staged image of one 64-key block of one KV group, the unit the selection /
+// window kernel copies global -> LDS.  It is the block's K and V^T as MFMA
+// fragments, K fragments first: fragment f < NFRAG is K subtile u = f / KS
+// (16 keys) at k step ks = f % KS; fragment NFRAG + 2 mt + h is V^T channel
+// tile mt (16 channels) over keys 32 h .. 32 h + 31.  A fragment is NV pieces
+// of 64 lanes x 16 bytes (lane l holds its 8 elements; fp32 needs two
+// pieces), so every piece is one contiguous 1 KB copy.  Inside a 32-key half,
+// MFMA row rho of K subtile u holds key 8 (rho / 4) + 4 (u % 2) + rho % 4: the
+// C layout of the two S^T subtiles of a half is then the B-operand layout of
+// P^T for that half.
+template <typename T, int D>
+struct KvImage {
+  static constexpr int NV = (int)sizeof(T) * 8 / 16;   // 16-byte pieces per lane fragment
+  static constexpr int EPV = 16 / (int)sizeof(T);      // elements per piece and lane
+  static constexpr int KS = D / 32;
+  static constexpr int NFRAG = D / 8;                  // fragments per operand (4 KS = 2 (D/16))
+  static constexpr int PIECES = 2 * NFRAG * NV;
+  static constexpr int BYTES = PIECES * 1024;
+  // key (0..63 within the block) in K fragment row rho (= lane % 16) of subtile u
+  static __device__ __forceinline__ int krow(int u, int rho) {
+    return 32 * (u >> 1) + 8 * (rho >> 2) + 4 * (u & 1) + (rho & 3);
+  }
+};
+
 // Work order for a 1-D grid over (batch * kv-group) x tiles.  Workgroups are
 // dealt to the 8 XCDs round-robin (XCD = id % 8), each XCD with its own L2.
 // When the number of (batch, group) pairs NBG divides 8 or is a multiple of

@@ -15,11 +15,12 @@ struct Shape {
 };
 
 // K1: mean-pool.  kc/vc [B][nc][Hkv][D] (nullable); vct [B][Hkv][D][ncp]
-// (nullable); vt [B][Hkv][D][T] (nullable); radius [B][Hkv][ncp] fp32
-// (nullable); kc_lo [B][nc][Hkv][D] residual of the rounded kc (bf16 only,
-// nullable).
+// (nullable); kvimg [B][Hkv][nc][KvImage<T, D>::BYTES] staged block images
+// (nullable); knorm [B][Hkv][nc] fp32, largest
+// key norm per block (nullable); kc_lo [B][nc][Hkv][D] residual of the
+// rounded kc (bf16 only, nullable).
 hipError_t launch_pool(bool is_bf16, const Shape& s, const void* k, const void* v, void* kc,
-                       void* vc, void* vct, void* vt, float* radius, void* kc_lo,
+                       void* vc, void* vct, void* kvimg, float* knorm, void* kc_lo,
                        hipStream_t st);
 
 // K2: compressed attention + importance + top-k.
@@ -30,10 +31,10 @@ hipError_t launch_cmp_select(bool is_bf16, const Shape& s, const void* q, const 
                              void* o_cmp, float* ubound, int32_t* indices, bool do_topk,
                              hipStream_t st);
 
-// K3: selection (forced + compacted free blocks) + window + gated combine.
+// K3: selection + window + gated combine.  knorm from K1 (required).
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
-                          const void* vt, const void* gates, const void* o_cmp,
-                          const float* ubound, const int32_t* indices, void* out, float* lse,
+                          const void* kvimg, const void* gates, const void* o_cmp,
+                          const float* knorm, const int32_t* indices, void* out, float* lse,
                           void* o_sel, hipStream_t st);
 
 // Backward (selection branch).

@@ -7,28 +7,34 @@
 // [SIC] "Sparsity is Cool", Method: window 512; Key claims: the first block is
 // always read.  Reading: one joint softmax over all selected tokens s <= t.
 //
-// One workgroup per (tile of P positions, KV group g, batch b).  Rows are
-// (position, head); each wave owns RW rows as NCG column groups of 16 lane
-// slots, and a row never leaves its (group, slot): both branch accumulators
-// live in registers (MFMA C layout of O^T: lane = row, registers = channels).
+// Work decomposition.  One workgroup per (tile of P positions, KV group g,
+// batch b); eight waves.  A row is one (position, head).  A column group is 16
+// rows: 16/G consecutive positions times the G heads of the group, i.e. one
+// MFMA column tile.  Each wave owns NCG column groups for the whole kernel:
+// their Q fragments and both branch accumulators (MFMA C layout of O^T: lane =
+// row, registers = channels) stay in registers.
 //
-// The kernel walks the key blocks 0 .. last (the own block of the tile's last
-// position) once.  Each block's K (64 x D) and V^T (D x 64) are staged in LDS
-// by the whole workgroup, double-buffered (the next block's global loads are in
-// flight while the current one is computed).  For every staged block:
-//   window     rows whose window t-W < s <= t meets the block: dense 16-row
-//              MFMA tiles, online softmax per row;
-//   selection  rows whose position selected the block (block 0, the own block
-//              and the top-k picks alike): a wave packs, per MFMA tile, at most
-//              one row per lane slot -- the positions sharing a slot are its
-//              NCG groups -- so a tile needs no data movement between lanes and
-//              each lane adds the tile's O^T into the accumulator of the group
-//              its row belongs to.  Probabilities use a fixed per-row reference
-//              m_ref = max(tau q.k_t, U - 64) (log2 units) where U (from K2)
-//              bounds every logit of the row's candidate blocks: terms never
-//              exceed 2^64 and the own key's term never underflows unless
-//              U - tau q.k_t > 164; a tile holding such a row first takes the
-//              exact maximum over its selected blocks (slower, exact path).
+// One reference per row for both softmaxes.  Every logit of row (t, h) obeys
+//   tau q.k_s * log2(e) <= U = tau log2(e) |q| max_s |k_s|      (Cauchy-Schwarz)
+// with the maximum over the keys of blocks 0 .. own (K1 stores each block's
+// largest key norm).  Both branches subtract m = max(tau log2(e) q.k_t, U - 64)
+// (log2 units): no term exceeds 2^64 and the own key -- attended by both
+// branches -- keeps a term >= 2^-100 unless U - tau log2(e) q.k_t > 164.  A
+// wave holding such a row first takes the exact maxima, one per branch, over
+// the keys each branch attends (slower path, rare).  Because the reference is
+// fixed, the accumulation over blocks is a plain sum: a block's QK^T product
+// and its exponentials serve both branches, and rows that do not attend a
+// block get a reference of +inf (probability exactly 0) instead of a mask.
+//
+// Key blocks j = first .. own(last position) are walked once.  Each block's
+// image -- its K (64 x D) and V^T (D x 64) in MFMA fragment order, written by
+// the pooling kernel (KvImage) -- is copied global -> LDS with contiguous 1 KB
+// global_load_lds pieces (no register staging; fragment reads from LDS are
+// contiguous 16 bytes per lane, so bank-conflict free) through a ring of two
+// groups of GB blocks: the next group's loads are in flight while a group is
+// computed, with one barrier per group.  A wave skips a block's math when none
+// of its column groups attends it.  The key order inside the image makes the C layout of S^T the
+// B-operand layout of P^T (no data movement between QK^T and PV).
 // Results are deterministic (no atomics).  At the end
 //   out = g_cmp o_cmp + g_sel acc_sel / l_sel + g_win acc_win / l_win
 // rounded once.
@@ -37,15 +43,40 @@
 #include "nsa_device.h"
 #include "nsa_launch.h"
 
+// Per-shape tuning (waves per workgroup, column groups per wave, K / V^T
+// fragments per LDS read batch): overridable for experiments.
+#ifndef NSA_K3_W64
+#define NSA_K3_W64 16
+#endif
+#ifndef NSA_K3_NCG64
+#define NSA_K3_NCG64 1
+#endif
+#ifndef NSA_K3_FCH64
+#define NSA_K3_FCH64 2
+#endif
+#ifndef NSA_K3_W128
+#define NSA_K3_W128 12
+#endif
+#ifndef NSA_K3_NCG128
+#define NSA_K3_NCG128 1
+#endif
+#ifndef NSA_K3_FCH128
+#define NSA_K3_FCH128 2
+#endif
+// LDS budget of the staging ring (bytes); the ring takes as many stages as fit
+#ifndef NSA_K3_RING_BYTES
+#define NSA_K3_RING_BYTES (144 * 1024)
+#endif
+
 namespace nsa {
 
 struct SelWinArgs {
   const void* q;
   const void* k;
-  const void* vt;
+  const void* kvimg;   // [B][Hkv][nc] staged K / V^T images of the blocks (KvImage)
   const void* gates;
   const void* o_cmp;
-  const float* ubound;
+  const float* knorm;  // [B][Hkv][nc] largest key norm of each block
   const int32_t* indices;
   void* out;
   float* lse;
@@ -54,387 +85,482 @@ struct SelWinArgs {
 
 template <typename T, int D, int G>
 struct K3Cfg {
-  // waves per workgroup and target rows per wave: both accumulators (selection
-  // and window, 2 * rows/16 * D/4 fp32 registers per lane) must fit in registers
-  static constexpr int NW = (sizeof(T) == 2 && D == 128) ? 8 : 4;
+  static constexpr bool WIDE = D == 128 || sizeof(T) == 4;
+  static constexpr int NW = WIDE ? NSA_K3_W128 : NSA_K3_W64;  // waves per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int RWT = (sizeof(T) == 2 && D == 128) ? 32 : 64;
-  static constexpr int P = (NW * RWT / G) < 128 ? (NW * RWT / G) : 128;  // positions per tile
-  static constexpr int R = P * G;                 // rows per tile
-  static constexpr int RW = R / NW;               // rows per wave
-  static constexpr int NCG = RW / 16;             // column groups per wave (1, 2 or 4)
-  static constexpr int NSG = 16 / G;              // lane-slot groups (one position each)
-  static constexpr int PW = RW / G;               // positions per wave = NCG * NSG
-  static constexpr int KS = D / 32;               // k-steps over the head dim
-  static constexpr int MT = D / 16;               // 16-channel tiles
-  static constexpr int QST = D + 8;               // LDS row stride (elements), Q and K tiles
-  static constexpr int VST = 64 + 8;              // LDS row stride (elements), V^T tile
-  static constexpr int KCH = 64 * D * (int)sizeof(T) / 16;  // 16-byte chunks per K block
-  static constexpr int CPT = KCH / NT > 0 ? KCH / NT : 1;   // chunks per thread (K and V each)
-  static_assert(RW % 16 == 0, "rows per wave");
-  static_assert(KCH % NT == 0, "staging split");
+  static constexpr int WGPC = NW >= 8 ? 1 : 8 / NW;  // workgroups per CU aimed at (launch bound)
+  // column groups per wave: more share every K / V^T fragment read but cost
+  // registers (occupancy)
+  static constexpr int NCG = WIDE ? NSA_K3_NCG128 : NSA_K3_NCG64;
+  static constexpr int NSG = 16 / G;              // positions per column group
+  static constexpr int PW = NCG * NSG;            // positions per wave
+  static constexpr int P = NW * PW;               // positions per workgroup
+  static constexpr int KS = D / 32;               // 32-element k steps over the head dim
+  static constexpr int MT = D / 16;               // 16-channel output tiles
+  typedef KvImage<T, D> Img;
+  static constexpr int NV = Img::NV;              // 16-byte pieces per lane fragment
+  static constexpr int EPV = Img::EPV;            // elements per piece and lane
+  static constexpr int NFRAG = Img::NFRAG;        // fragments per operand and block (4 KS = 2 MT)
+  static constexpr int FCH_ = WIDE ? NSA_K3_FCH128 : NSA_K3_FCH64;
+  static constexpr int FCH = (NFRAG < FCH_ ? NFRAG : FCH_) / NV;  // fragments per LDS read batch
+  static constexpr int FRAG_BYTES = NV * 1024;
+  static constexpr int STAGE = Img::BYTES;        // one block's image: K fragments, then V^T
+  // blocks per barrier group; the ring holds two groups (about 128 KB)
+  static constexpr int GB = (NSA_K3_RING_BYTES / STAGE / 2) < 4 ? (NSA_K3_RING_BYTES / STAGE / 2) : 4;
+  static constexpr int NBUF = 2 * GB;
+  static_assert(GB >= 1, "ring too small");
+  static constexpr int LOADS = 2 * NFRAG * NV;    // 1 KB global->LDS loads per stage
+  static_assert(NSG * G == 16, "column group = 16 rows");
 };
 
 template <typename T, int D, int G>
 static size_t k3_lds_bytes(int topk) {
   typedef K3Cfg<T, D, G> C;
-  return sizeof(T) * ((size_t)2 * 64 * C::QST + (size_t)2 * D * C::VST + (size_t)C::R * C::QST) +
-         (size_t)C::P * topk * 2 + 16;
+  return (size_t)C::NBUF * C::STAGE + (size_t)C::P * topk * 2;
 }
 
-// 16-byte vector of T
-template <typename T> struct V16;
-template <> struct V16<bf16> { typedef bf16x8 type; };
-template <> struct V16<float> { typedef f32x4 type; };
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier that is also a compiler memory barrier but, unlike
+// __syncthreads, does not drain the outstanding global->LDS loads.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// lane fragment (8 elements) stored as [NV][64 lanes][16 bytes] in LDS
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type lds_frag(const unsigned char* base, int l);
+template <>
+__device__ __forceinline__ bf16x8 lds_frag<bf16>(const unsigned char* base, int l) {
+  return *reinterpret_cast<const bf16x8*>(base + 16 * l);
+}
+template <>
+__device__ __forceinline__ f32x8 lds_frag<float>(const unsigned char* base, int l) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(base + 16 * l);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(base + 1024 + 16 * l);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+  return r;
+}
+
+// Sum of the 8 probabilities of a B fragment (the values the PV MFMA uses).
+__device__ __forceinline__ float frag_sum(const bf16x8& p) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {p[2 * i], p[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& p) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += p[i];
+  return s;
+}
+// lanes whose condition is false get an all-zero fragment
+__device__ __forceinline__ bf16x8 frag_keep(const bf16x8& p, bool keep) {
+  typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+  u32x4 u = __builtin_bit_cast(u32x4, p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = keep ? u[i] : 0u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f32x8 frag_keep(const f32x8& p, bool keep) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = keep ? p[i] : 0.f;
+  return r;
+}
+
+// minimum over each 16-lane row (DPP butterfly; every lane gets its row's minimum)
+__device__ __forceinline__ int row_min16(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true));  // other quad of 8
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true));  // other half of 16
+  return v;
+}
+
+// key (0..63 within the block) of C-layout element (subtile u, register r) in lane group a
+__device__ __forceinline__ int key_of(int u, int a, int r) { return 32 * (u >> 1) + 8 * a + 4 * (u & 1) + r; }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__((K3Cfg<T, D, G>::NT)) void sel_win_kernel(Shape s, SelWinArgs args) {
+__global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void sel_win_kernel(Shape s, SelWinArgs args) {
   typedef K3Cfg<T, D, G> C;
-  constexpr int NT = C::NT, P = C::P, R = C::R, NCG = C::NCG, NSG = C::NSG;
-  constexpr int PW = C::PW, KS = C::KS, MT = C::MT, QST = C::QST, VST = C::VST, CPT = C::CPT;
+  constexpr int NT = C::NT, P = C::P, NCG = C::NCG, NSG = C::NSG, PW = C::PW;
+  constexpr int KS = C::KS, MT = C::MT, NV = C::NV, EPV = C::EPV, NFRAG = C::NFRAG, FCH = C::FCH;
+  constexpr int FRAG_BYTES = C::FRAG_BYTES, STAGE = C::STAGE, NBUF = C::NBUF, GB = C::GB, LOADS = C::LOADS;
   typedef typename Frag<T>::type FragT;
-  typedef typename V16<T>::type Vec;
-  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  const float INF = __builtin_inff();
 
   const T* __restrict__ q = (const T*)args.q;
   const T* __restrict__ k = (const T*)args.k;
-  const T* __restrict__ vt = (const T*)args.vt;
 
   const int NTL = (s.T + P - 1) / P;
   int bg, tile;
   xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
   const int g = bg % s.Hkv, b = bg / s.Hkv;
   const int t0 = tile * P;
-  const int nvalid = min(P, s.T - t0);  // the last tile may be ragged (T % P != 0)
-  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int nvalid = min(P, s.T - t0);  // the last tile may be ragged
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int l = threadIdx.x % kWave;
   const int a = l / 16, col = l % 16;
-  const int sg = col / G, hh = col % G;  // lane slot -> slot group, head
+  const int sg = col / G, hh = col % G;
+  const int h = g * G + hh;
   const float c1 = s.scale * kLog2e;
   const bool sel_on = !(s.flags & 2u);
   const bool cmp_on = !(s.flags & 1u);
   const bool win_on = !(s.flags & 4u);
   const bool need_sel = sel_on || args.lse != nullptr || args.o_sel != nullptr;
   const int topk = s.topk;
+  const int W = s.W;
 
   const size_t k_row = (size_t)s.Hkv * D;
   const T* k_b = k + (size_t)b * s.T * k_row + (size_t)g * D;
-  const T* vt_b = vt + ((size_t)b * s.Hkv + g) * (size_t)D * s.T;
+  const unsigned char* img_b =
+      (const unsigned char*)args.kvimg + ((size_t)b * s.Hkv + g) * s.nc * (size_t)STAGE;
   const size_t q_row = (size_t)s.Hq * D;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  T* Kl = reinterpret_cast<T*>(smem);             // [2][64][QST]
-  T* Vl = Kl + 2 * 64 * QST;                      // [2][D][VST]
-  T* Ql = Vl + 2 * D * VST;                       // [R][QST]
-  int16_t* lists = reinterpret_cast<int16_t*>(Ql + (size_t)R * QST);  // [P][topk]
-  int* flag = reinterpret_cast<int*>(lists + P * topk);
+  unsigned char* ring = smem;                                          // [NBUF][STAGE]
+  int16_t* lists = reinterpret_cast<int16_t*>(smem + (size_t)NBUF * STAGE);  // [P][topk]
 
-  // ---------------------------------------------------------------- setup
-  // Q tile (rows (p, hh), positions t0 .. t0+P-1) -> LDS
-  {
-    constexpr int QCH = R * D / EPV;
-    for (int i = threadIdx.x; i < QCH; i += NT) {
-      const int r = i / (D / EPV), c8 = i % (D / EPV);
-      const int p = r / G, h2 = r % G;
-      Vec v;
-      if (p < nvalid) {
-        v = *reinterpret_cast<const Vec*>(q + ((size_t)b * s.T + t0 + p) * q_row +
-                                          (size_t)(g * G + h2) * D + c8 * EPV);
-      } else {
-        for (int e = 0; e < EPV; ++e) v[e] = (T)0.f;
-      }
-      *reinterpret_cast<Vec*>(Ql + (size_t)r * QST + c8 * EPV) = v;
-    }
-  }
+  // ------------------------------------------------------------ setup
   if (need_sel) {
     for (int i = threadIdx.x; i < P * topk; i += NT) {
       const int p = i / topk, e = i % topk;
-      const int j =
-          p < nvalid ? args.indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e] : -1;
+      const int j = p < nvalid ? args.indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e] : -1;
       lists[i] = (int16_t)(j < 0 ? 0x7fff : j);  // block indices are < 1024
     }
   }
-  if (threadIdx.x == 0) *flag = 0;
-
-  // staging of block j: global -> registers (fetch), registers -> LDS (commit)
-  Vec kreg[CPT], vreg[CPT];
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = threadIdx.x + i * NT;
-      const int kr = ci / (D / EPV), kc = ci % (D / EPV);
-      kreg[i] = *reinterpret_cast<const Vec*>(k_b + (size_t)(j * kBlock + kr) * k_row + kc * EPV);
-      const int vr = ci / (kBlock / EPV), vc = ci % (kBlock / EPV);
-      vreg[i] = *reinterpret_cast<const Vec*>(vt_b + (size_t)vr * s.T + j * kBlock + vc * EPV);
-    }
-  };
-  auto commit = [&](int bf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = threadIdx.x + i * NT;
-      const int kr = ci / (D / EPV), kc = ci % (D / EPV);
-      *reinterpret_cast<Vec*>(Kl + (size_t)(bf * 64 + kr) * QST + kc * EPV) = kreg[i];
-      const int vr = ci / (kBlock / EPV), vc = ci % (kBlock / EPV);
-      *reinterpret_cast<Vec*>(Vl + (size_t)(bf * D + vr) * VST + vc * EPV) = vreg[i];
-    }
-  };
 
   const int c_last = (t0 + nvalid - 1) / kBlock;
-  const int j_win0 = win_on ? max(0, t0 - s.W + 1) / kBlock : c_last + 1;
-  const int j_begin = need_sel ? 0 : j_win0;
+  // largest key norm over blocks 0 .. c_last (every wave reduces it itself)
+  float mk = 0.f;
+  {
+    const float* kn = args.knorm + ((size_t)b * s.Hkv + g) * s.nc;
+    for (int j = l; j <= c_last; j += kWave) mk = fmaxf(mk, kn[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mk = fmaxf(mk, __shfl_xor(mk, o));
+  }
 
-  __syncthreads();
-
-  // per-lane row bookkeeping: lane slot col, group cg -> position / row
-  float m_ref[NCG], l_sel[NCG], m_w[NCG], l_w[NCG];
-  int ptr[NCG], nxt[NCG];
-  f32x4 acc_sel[NCG][MT], acc_win[NCG][MT];
+  // per column group: this lane's row
+  int tpos[NCG], own[NCG], nxt[NCG], ptr[NCG];
+  bool valid[NCG];
+  FragT qf[NCG][KS];
+  float mr_s[NCG], mr_w[NCG];  // references (log2 units) of the two softmaxes
+  bool any_exact = false;
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    m_ref[cg] = 0.f;
-    l_sel[cg] = 0.f;
-    m_w[cg] = -INFINITY;
-    l_w[cg] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) { acc_sel[cg][mt] = zero4(); acc_win[cg][mt] = zero4(); }
-    const int p = w * PW + cg * NSG + sg;
+    const int p0 = w * PW + cg * NSG;
+    const int p = p0 + sg;
+    tpos[cg] = t0 + p;
+    own[cg] = (t0 + p0) / kBlock;  // NSG divides 64: one own block per column group
+    valid[cg] = p < nvalid;
     ptr[cg] = 0;
-    nxt[cg] = need_sel ? lists[p * topk] : 0x7fff;
-  }
-
-  auto qfrag = [&](int row, int ks) -> FragT {
-    return Frag<T>::load(Ql + (size_t)row * QST + ks * 32 + a * 8);
-  };
-
-  // reference maximum per row: tau q.k_t (the own key, always selected), U - 64
-  if (need_sel) {
-    int any_flag = 0;
+    float qq = 0.f, d = 0.f;
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      const int p = w * PW + cg * NSG + sg;
-      if (p >= nvalid) continue;
-      const int t = t0 + p, h = g * G + hh;
-      const T* krow = k_b + (size_t)t * k_row;
-      float d = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      if (valid[cg]) {
+        qf[cg][ks] = Frag<T>::load(q + ((size_t)b * s.T + tpos[cg]) * q_row + (size_t)h * D + ks * 32 + 8 * a);
+        const FragT kv = Frag<T>::load(k_b + (size_t)tpos[cg] * k_row + ks * 32 + 8 * a);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const FragT qv = qfrag(p * G + hh, ks);
-        const FragT kv = Frag<T>::load(krow + ks * 32 + a * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += (float)qv[e] * (float)kv[e];
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qf[cg][ks][e];
+          qq += x * x;
+          d += x * (float)kv[e];
+        }
+      } else {
+        qf[cg][ks] = Frag<T>::zero();
       }
-      const float mdiag = xsum4(d) * c1;
-      const float ub = args.ubound[((size_t)b * s.Hq + h) * s.T + t];
-      m_ref[cg] = fmaxf(mdiag, ub - 64.f);
-      any_flag |= (ub - mdiag > 164.f) ? 1 : 0;
     }
-    if (any_flag) atomicOr(flag, 1);
+    qq = xsum4(qq);
+    d = xsum4(d);
+    const float mdiag = d * c1;
+    const float ub = c1 * sqrtf(qq) * mk * (1.0f + 1e-6f);
+    const float m = fmaxf(mdiag, ub - 64.f);
+    mr_s[cg] = valid[cg] ? m : INF;
+    mr_w[cg] = mr_s[cg];
+    any_exact |= valid[cg] && (ub - mdiag > 164.f);
   }
-  __syncthreads();
-  const bool exact_pass = need_sel && (*flag != 0);
-
-  // ------------------------------------------------- exact maxima (rare path)
-  if (exact_pass) {
-    float m_ex[NCG];
-    int eptr[NCG], enx[NCG];
+  __syncthreads();  // lists visible
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) { m_ex[cg] = -INFINITY; eptr[cg] = 0; enx[cg] = nxt[cg]; }
-    for (int j = 0; j <= c_last; ++j) {
-      fetch(j);
-      commit(0);
-      __syncthreads();
-      int gm = 0;
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int p = w * PW + cg * NSG + sg;
+    nxt[cg] = (need_sel && valid[cg]) ? lists[p * topk] : 0x7fff;
+  }
+  // Wave-uniform activity of each column group (lanes 0..15 hold its 16 rows):
+  //   nsel   next block any of its rows selected (0x7fff: none left);
+  //   window blocks jw_lo .. jw_hi meet some row's window; blocks <= jw_edge
+  //          hold keys at or below t - W for some row (partial window block).
+  int nsel[NCG], jw_lo[NCG], jw_hi[NCG], jw_edge[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    nsel[cg] = __builtin_amdgcn_readfirstlane(row_min16(nxt[cg]));
+    const int pf = w * PW + cg * NSG;  // first position of the column group
+    const int nv = min(max(nvalid - pf, 0), NSG);
+    const int tf = t0 + pf, tl = tf + nv - 1;
+    if (win_on && nv > 0) {
+      jw_lo[cg] = max(0, tf - W + 1) / kBlock;
+      jw_hi[cg] = tf / kBlock;
+      jw_edge[cg] = tl >= W ? (tl - W) / kBlock : -1;
+    } else {
+      jw_lo[cg] = 1;
+      jw_hi[cg] = 0;
+      jw_edge[cg] = -1;
+    }
+  }
+
+  // ------------------------------------------ exact maxima (rare; per wave)
+  // The wave reads the K fragments straight from global memory; no barriers.
+  const bool exact = __builtin_amdgcn_ballot_w64(any_exact) != 0;
+  if (exact) {
+    float ms[NCG], mw[NCG];
+    int ep[NCG], en[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) { ms[cg] = -INF; mw[cg] = -INF; ep[cg] = 0; en[cg] = nxt[cg]; }
+    const int jw0 = win_on ? max(0, t0 - W + 1) / kBlock : c_last + 1;
+    for (int j = need_sel ? 0 : jw0; j <= c_last; ++j) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        if (enx[cg] == j) {
-          gm |= 1 << cg;
-          ++eptr[cg];
+        const int t = tpos[cg];
+        const bool sl = en[cg] == j;
+        if (sl) {
+          ++ep[cg];
           const int p = w * PW + cg * NSG + sg;
-          enx[cg] = eptr[cg] < topk ? lists[p * topk + eptr[cg]] : 0x7fff;
+          en[cg] = ep[cg] < topk ? lists[p * topk + ep[cg]] : 0x7fff;
+        }
+        const bool wl = win_on && valid[cg] && j * kBlock <= t && j * kBlock + kBlock - 1 > t - W;
+        if (__builtin_amdgcn_ballot_w64(sl || wl) == 0) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int krow = KvImage<T, D>::krow(u, col);
+          f32x4 st = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            st = mma(st, Frag<T>::load(k_b + (size_t)(j * kBlock + krow) * k_row + ks * 32 + 8 * a),
+                     qf[cg][ks]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = j * kBlock + key_of(u, a, r);
+            const float x = st[r] * c1;
+            if (sl && key <= t) ms[cg] = fmaxf(ms[cg], x);
+            if (wl && key <= t && key > t - W) mw[cg] = fmaxf(mw[cg], x);
+          }
         }
       }
-      const int cnt = __popc(gm);
-      for (int tt = 0; __builtin_amdgcn_ballot_w64(tt < cnt) != 0; ++tt) {
-        int rem = gm;
-        for (int z = 0; z < tt; ++z) rem &= rem - 1;
-        const int cgt = rem ? __ffs(rem) - 1 : 0;
-        const bool valid = tt < cnt;
-        const int p = w * PW + cgt * NSG + sg;
-        const int t = t0 + p;
-        FragT qf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = qfrag(p * G + hh, ks);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int krow = cc * 32 + 8 * (col / 4) + 4 * u + (col % 4);
-            f32x4 st = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-              st = mma(st, Frag<T>::load(Kl + (size_t)krow * QST + ks * 32 + a * 8), qf[ks]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * kBlock + cc * 32 + 8 * a + 4 * u + r;
-              if (key <= t) mx = fmaxf(mx, st[r] * c1);
-            }
-          }
-        mx = xmax4(mx);
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          if (valid && cg == cgt) m_ex[cg] = fmaxf(m_ex[cg], mx);
-      }
-      __syncthreads();
     }
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) m_ref[cg] = m_ex[cg];
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float a1 = xmax4(ms[cg]), a2 = xmax4(mw[cg]);
+      if (valid[cg]) {
+        if (need_sel) mr_s[cg] = a1;
+        if (win_on) mr_w[cg] = a2;
+      }
+    }
   }
 
   // ------------------------------------------------------------ main walk
-  if (j_begin <= c_last) {
-    fetch(j_begin);
-    commit(0);
+  const int j_win0 = win_on ? max(0, t0 - W + 1) / kBlock : c_last + 1;
+  const int j_begin = need_sel ? 0 : j_win0;
+  const int nblk = c_last - j_begin + 1;
+
+  // stage loads: this wave's 1 KB pieces (w, w + NW, ...) of block j's image
+  // into ring slot bf; lane l copies its 16 bytes of a piece
+  auto issue = [&](int j, int bf) {
+    unsigned char* stage = ring + (size_t)bf * STAGE;
+    const unsigned char* src = img_b + (size_t)j * STAGE + 16 * l;
+    for (int pc = w; pc < LOADS; pc += C::NW)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024),
+                                       (void*)(stage + (size_t)pc * 1024), 16, 0, 0);
+  };
+
+  float l_s[NCG], l_w[NCG];
+  f32x4 acc_s[NCG][MT], acc_w[NCG][MT];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    l_s[cg] = 0.f;
+    l_w[cg] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { acc_s[cg][mt] = zero4(); acc_w[cg][mt] = zero4(); }
   }
-  __syncthreads();
-  for (int j = j_begin; j <= c_last; ++j) {
-    const int bf = (j - j_begin) & 1;
-    const bool more = j < c_last;
-    if (more) fetch(j + 1);
-    const T* Kb = Kl + (size_t)bf * 64 * QST;
-    const T* Vb = Vl + (size_t)bf * D * VST;
 
-    // ---------------- window: dense tiles over this wave's rows
-    if (j >= j_win0) {
+  // The ring holds two groups of GB blocks: while one group is computed the
+  // next one is in flight.  One barrier per group (not per block) lets each
+  // wave's uneven per-block work average out over the group.
+  const int ngrp = (nblk + GB - 1) / GB;
+  auto issue_group = [&](int gi) {
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        const int p = w * PW + cg * NSG + sg;
-        const int t = t0 + p;
-        if (__builtin_amdgcn_ballot_w64(j * kBlock <= t && j * kBlock + kBlock - 1 > t - s.W) == 0)
-          continue;  // block outside every window of this column group
-        FragT qf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = qfrag(p * G + hh, ks);
-        float x[2][8];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int krow = cc * 32 + 8 * (col / 4) + 4 * u + (col % 4);
-            f32x4 st = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-              st = mma(st, Frag<T>::load(Kb + (size_t)krow * QST + ks * 32 + a * 8), qf[ks]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * kBlock + cc * 32 + 8 * a + 4 * u + r;
-              x[cc][4 * u + r] = (key <= t && key > t - s.W) ? st[r] * c1 : -INFINITY;
-            }
-          }
-        float mx = x[0][0];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[cc][e]);
-        mx = xmax4(mx);
-        const float mn = fmaxf(m_w[cg], mx);
-        float alpha = 1.f, psum = 0.f;
-        float pv[2][8];
-        if (mn == -INFINITY) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[cc][e] = 0.f;
-        } else {
-          alpha = fast_exp2(m_w[cg] - mn);
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { pv[cc][e] = fast_exp2(x[cc][e] - mn); psum += pv[cc][e]; }
-        }
-        l_w[cg] = l_w[cg] * alpha + xsum4(psum);
-        m_w[cg] = mn;
-        const FragT pf0 = Frag<T>::from_f32(pv[0]);
-        const FragT pf1 = Frag<T>::from_f32(pv[1]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const T* vrow = Vb + (size_t)(mt * 16 + col) * VST + 8 * a;
-          f32x4 o = acc_win[cg][mt] * alpha;
-          o = mma(o, Frag<T>::load(vrow), pf0);
-          acc_win[cg][mt] = mma(o, Frag<T>::load(vrow + 32), pf1);
-        }
-      }
-    }
+    for (int q = 0; q < GB; ++q)
+      if (gi * GB + q < nblk) issue(j_begin + gi * GB + q, (gi & 1) * GB + q);
+  };
+  issue_group(0);
 
-    // ---------------- selection: slot-packed tiles of the rows that chose j
-    if (need_sel) {
-      int gm = 0;
+  for (int gi = 0; gi < ngrp; ++gi) {
+    wait_vmcnt<0>();       // this wave's loads of group gi (the only ones in flight)
+    barrier_keep_loads();  // all of group gi is in LDS; group gi-1's slots are free
+    if (gi + 1 < ngrp) issue_group(gi + 1);
+  for (int q = 0; q < GB; ++q) {
+    const int r = gi * GB + q;
+    if (r >= nblk) break;
+    const int j = j_begin + r;
+    const unsigned char* stage = ring + (size_t)((gi & 1) * GB + q) * STAGE;
+
+    // which rows attend block j: scalar tests per column group, per-lane
+    // tests only for the groups that attend it
+    bool sl[NCG], wl[NCG], act_s[NCG], act_w[NCG], act[NCG], wlow[NCG];
+    bool any = false;
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        if (nxt[cg] == j) {
-          gm |= 1 << cg;
+    for (int cg = 0; cg < NCG; ++cg) {
+      act_s[cg] = j == nsel[cg];
+      act_w[cg] = j >= jw_lo[cg] && j <= jw_hi[cg];
+      wlow[cg] = act_w[cg] && j <= jw_edge[cg];
+      act[cg] = act_s[cg] || act_w[cg];
+      any |= act[cg];
+      sl[cg] = false;
+      wl[cg] = false;
+      if (act_s[cg]) {
+        sl[cg] = nxt[cg] == j;
+        if (sl[cg]) {
           ++ptr[cg];
           const int p = w * PW + cg * NSG + sg;
           nxt[cg] = ptr[cg] < topk ? lists[p * topk + ptr[cg]] : 0x7fff;
         }
+        nsel[cg] = __builtin_amdgcn_readfirstlane(row_min16(nxt[cg]));
       }
-      const int cnt = __popc(gm);
-      for (int tt = 0; __builtin_amdgcn_ballot_w64(tt < cnt) != 0; ++tt) {
-        int rem = gm;
-        for (int z = 0; z < tt; ++z) rem &= rem - 1;
-        const int cgt = rem ? __ffs(rem) - 1 : 0;
-        const bool valid = tt < cnt;
-        const int p = w * PW + cgt * NSG + sg;
-        const int t = t0 + p;
-        float mr = m_ref[0];
+      if (act_w[cg]) {
+        const int t = tpos[cg];
+        wl[cg] = valid[cg] && j * kBlock <= t && j * kBlock + kBlock - 1 > t - W;
+      }
+    }
+    if (!any) continue;
+
+    // S^T = K Q^T for the active column groups.  The K fragments are read from
+    // LDS in chunks of up to 8, all loads of a chunk issued before the first
+    // MFMA, and each fragment serves every active column group.
+    f32x4 st[NCG][4];
 #pragma unroll
-        for (int cg = 1; cg < NCG; ++cg) mr = (cg == cgt) ? m_ref[cg] : mr;
-        FragT qf[KS];
+    for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = qfrag(p * G + hh, ks);
-        float pv[2][8];
-        float psum = 0.f;
+      for (int u = 0; u < 4; ++u) st[cg][u] = zero4();
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+    for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
+      FragT kf[FCH];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int krow = cc * 32 + 8 * (col / 4) + 4 * u + (col % 4);
-            f32x4 st = zero4();
+      for (int i = 0; i < FCH; ++i) kf[i] = lds_frag<T>(stage + (size_t)(f0 + i) * FRAG_BYTES, l);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-              st = mma(st, Frag<T>::load(Kb + (size_t)krow * QST + ks * 32 + a * 8), qf[ks]);
+      for (int cg = 0; cg < NCG; ++cg) {
+        if (!act[cg]) continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * kBlock + cc * 32 + 8 * a + 4 * u + r;
-              const float e = (valid && key <= t) ? fast_exp2(st[r] * c1 - mr) : 0.f;
-              pv[cc][4 * u + r] = e;
-              psum += e;
-            }
-          }
-        psum = xsum4(psum);
-        const FragT pf0 = Frag<T>::from_f32(pv[0]);
-        const FragT pf1 = Frag<T>::from_f32(pv[1]);
-        float msk[NCG];
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          msk[cg] = (valid && cg == cgt) ? 1.f : 0.f;
-          l_sel[cg] += msk[cg] * psum;
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const T* vrow = Vb + (size_t)(mt * 16 + col) * VST + 8 * a;
-          f32x4 o = zero4();
-          o = mma(o, Frag<T>::load(vrow), pf0);
-          o = mma(o, Frag<T>::load(vrow + 32), pf1);
-#pragma unroll
-          for (int cg = 0; cg < NCG; ++cg) acc_sel[cg][mt] += o * msk[cg];
+        for (int i = 0; i < FCH; ++i) {
+          const int u = (f0 + i) / KS, ks = (f0 + i) % KS;
+          st[cg][u] = mma(st[cg][u], kf[i], qf[cg][ks]);
         }
       }
     }
 
-    // the other buffer held block j - 1, which every wave finished before the
-    // barrier that ended the previous iteration
-    if (more) commit(bf ^ 1);
-    __syncthreads();
+    // first chunk of V^T fragments: issued now, in flight during the softmax
+    FragT vf0[FCH];
+#pragma unroll
+    for (int i = 0; i < FCH; ++i) vf0[i] = lds_frag<T>(stage + (size_t)(NFRAG + i) * FRAG_BYTES, l);
+
+    // probabilities, per branch, as PV B fragments (one per 32-key half).
+    // Blocks strictly inside every row's range (no causal diagonal, no window
+    // edge) take a mask-free path; rows that do not attend get reference +inf.
+    FragT ps[NCG][2], pw[NCG][2];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      if (!act[cg]) continue;
+      const int t = tpos[cg];
+      const bool diag = j == own[cg];
+      const bool dual = exact && act_s[cg] && act_w[cg];  // two references only after the exact pass
+      if (!diag && !wlow[cg] && !dual) {
+        const bool both = act_s[cg] && act_w[cg];
+        const bool att = act_s[cg] ? sl[cg] : wl[cg];
+        const float mr = (both ? (sl[cg] || wl[cg]) : att) ? mr_s[cg] : INF;  // mr_s == mr_w here
+        FragT pf[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(st[cg][2 * hf + e / 4][e % 4] * c1 - mr);
+          pf[hf] = Frag<T>::from_f32(pv);
+        }
+        if (both) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            ps[cg][hf] = frag_keep(pf[hf], sl[cg]);
+            pw[cg][hf] = frag_keep(pf[hf], wl[cg]);
+          }
+          l_s[cg] += frag_sum(ps[cg][0]) + frag_sum(ps[cg][1]);
+          l_w[cg] += frag_sum(pw[cg][0]) + frag_sum(pw[cg][1]);
+        } else if (act_s[cg]) {
+          ps[cg][0] = pf[0];
+          ps[cg][1] = pf[1];
+          l_s[cg] += frag_sum(pf[0]) + frag_sum(pf[1]);
+        } else {
+          pw[cg][0] = pf[0];
+          pw[cg][1] = pf[1];
+          l_w[cg] += frag_sum(pf[0]) + frag_sum(pf[1]);
+        }
+      } else {
+        // causal diagonal, window edge, or rows with two exact references
+        const float ms = sl[cg] ? mr_s[cg] : INF, mw = wl[cg] ? mr_w[cg] : INF;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8], qw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 2 * hf + e / 4, rr = e % 4;
+            const float x = st[cg][u][rr] * c1;
+            const int key = j * kBlock + key_of(u, a, rr);
+            const bool caus = key <= t;
+            pv[e] = caus ? fast_exp2(x - ms) : 0.f;
+            qw[e] = (caus && key > t - W) ? fast_exp2(x - mw) : 0.f;
+          }
+          ps[cg][hf] = Frag<T>::from_f32(pv);
+          pw[cg][hf] = Frag<T>::from_f32(qw);
+        }
+        if (act_s[cg]) l_s[cg] += frag_sum(ps[cg][0]) + frag_sum(ps[cg][1]);
+        if (act_w[cg]) l_w[cg] += frag_sum(pw[cg][0]) + frag_sum(pw[cg][1]);
+      }
+    }
+
+    // O^T += V^T P^T; V^T fragments in chunks as above, each read once
+#pragma unroll
+    for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
+      FragT vf[FCH];
+#pragma unroll
+      for (int i = 0; i < FCH; ++i)
+        vf[i] = f0 == 0 ? vf0[i] : lds_frag<T>(stage + (size_t)(NFRAG + f0 + i) * FRAG_BYTES, l);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        if (act_s[cg]) {
+#pragma unroll
+          for (int i = 0; i < FCH; ++i) {
+            const int mt = (f0 + i) / 2, hf = (f0 + i) % 2;
+            acc_s[cg][mt] = mma(acc_s[cg][mt], vf[i], ps[cg][hf]);
+          }
+        }
+        if (act_w[cg]) {
+#pragma unroll
+          for (int i = 0; i < FCH; ++i) {
+            const int mt = (f0 + i) / 2, hf = (f0 + i) % 2;
+            acc_w[cg][mt] = mma(acc_w[cg][mt], vf[i], pw[cg][hf]);
+          }
+        }
+      }
+    }
+  }
   }
 
   // ------------------------------------------------------------ combine
@@ -442,30 +568,29 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT)) void sel_win_kernel(Shape s, 
   T* out = (T*)args.out;
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const int p = w * PW + cg * NSG + sg;
-    if (p >= nvalid) continue;
-    const int t = t0 + p, h = g * G + hh;
+    const float ls = xsum4(l_s[cg]), lw = xsum4(l_w[cg]);
+    if (!valid[cg]) continue;
+    const int t = tpos[cg];
     const T* grow = gates + (((size_t)b * s.T + t) * s.Hq + h) * 3;
     const float gc = cmp_on ? to_f32(grow[0]) : 0.f;
     const float gs = sel_on ? to_f32(grow[1]) : 0.f;
     const float gw = win_on ? to_f32(grow[2]) : 0.f;
-    const float iw = win_on ? gw / l_w[cg] : 0.f;
-    const float il = need_sel ? 1.f / l_sel[cg] : 0.f;
+    const float iw = win_on ? gw / lw : 0.f;
+    const float il = need_sel ? 1.f / ls : 0.f;
     const size_t obase = ((size_t)b * s.T + t) * q_row + (size_t)h * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int d0 = mt * 16 + 4 * a;
-      f32x4 res = acc_win[cg][mt] * iw;
+      f32x4 res = acc_w[cg][mt] * iw;
       if (need_sel) {
-        const f32x4 os = acc_sel[cg][mt] * il;
+        const f32x4 os = acc_s[cg][mt] * il;
         if (sel_on) res += os * gs;
         if (args.o_sel) store4((T*)args.o_sel + obase + d0, os);
       }
       if (cmp_on && t >= kBlock - 1) res += load4((const T*)args.o_cmp + obase + d0) * gc;
       store4(out + obase + d0, res);
     }
-    if (args.lse && a == 0)
-      args.lse[((size_t)b * s.Hq + h) * s.T + t] = (m_ref[cg] + __log2f(l_sel[cg])) * kLn2;
+    if (args.lse && a == 0) args.lse[((size_t)b * s.Hq + h) * s.T + t] = (mr_s[cg] + __log2f(ls)) * kLn2;
   }
 }
 
@@ -495,10 +620,10 @@ static hipError_t launch_sw_g(const Shape& s, const SelWinArgs& a, hipStream_t s
 }
 
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
-                          const void* vt, const void* gates, const void* o_cmp,
-                          const float* ubound, const int32_t* indices, void* out, float* lse,
+                          const void* kvimg, const void* gates, const void* o_cmp,
+                          const float* knorm, const int32_t* indices, void* out, float* lse,
                           void* o_sel, hipStream_t st) {
-  SelWinArgs a{q, k, vt, gates, o_cmp, ubound, indices, out, lse, o_sel};
+  SelWinArgs a{q, k, kvimg, gates, o_cmp, knorm, indices, out, lse, o_sel};
   if (is_bf16) {
     if (s.D == 64) return launch_sw_g<bf16, 64>(s, a, st);
     return launch_sw_g<bf16, 128>(s, a, st);

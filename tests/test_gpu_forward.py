@@ -10,6 +10,14 @@ from sparse_attention_long_compress_amd.synth import WORKLOADS, Workload
 from tests.nsa_cases import (assert_close, check_indices, device_inputs, gpu_forward,
                              oracle_forward, rows_mask_from_groups, to_np)
 
+# Saved log-sum-exp of the selection softmax.  The library normalises with the
+# sum of the bf16-rounded probabilities it feeds to the PV product (so that the
+# output is an exact weighted average of those weights); each term carries a
+# relative rounding error <= 2^-8 (bf16 unit roundoff), so the sum is off by
+# <= 2^-8 relative and lse by <= ln(1 + 2^-8) ~ 3.90e-3, plus fp32 summation
+# error far below that.  fp32 inputs keep fp32 probabilities.
+LSE_TOL = {"bf16": 4e-3, "fp32": 1e-5}
+
 pytestmark = pytest.mark.gpu
 
 
@@ -110,7 +118,7 @@ def test_forward_matches_oracle(name, T, planted, over):
     assert_close(to_np(res["out"])[rows], ora["out"][rows], wl.dtype, "out")
     assert_close(to_np(res["o_sel"])[rows], ora["o_sel"][rows], wl.dtype, "o_sel")
     lse_rows = np.transpose(rows, (0, 2, 1))
-    lse_tol = 1e-3 if wl.dtype == "bf16" else 1e-5
+    lse_tol = LSE_TOL[wl.dtype]
     err = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"])[lse_rows]
     assert err.max() < lse_tol, err.max()
 
@@ -125,7 +133,7 @@ def test_forward_with_oracle_indices_every_row():
     torch.cuda.synchronize()
     assert_close(to_np(res["out"]), ora["out"], "bf16", "out")
     assert_close(to_np(res["o_sel"]), ora["o_sel"], "bf16", "o_sel")
-    assert np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"]).max() < 1e-3
+    assert np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"]).max() < LSE_TOL[wl.dtype]
     assert torch.equal(idx.cpu(), torch.from_numpy(ora["indices"]))  # input left untouched
 
 
