@@ -60,23 +60,114 @@ def algorithmic_bytes(wl):
     return es * (B * T * Hq * D * 2 + 2 * B * T * Hkv * D + B * T * Hq * 3)
 
 
-def cpu_baseline(wl, arrs_f64, budget_rows=None):
-    import numpy as np
+def oracle_threads():
+    """Host threads for the oracle: the cores this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return int(os.environ.get("NSA_ORACLE_THREADS", "0")) or max(1, min(16, n))
 
+
+def cpu_baseline(wl, arrs_f64, min_seconds=10.0, max_passes=50):
+    """The fp64 oracle on the host: whole forward passes of the same workload,
+    repeated until at least min_seconds of CPU time have been measured."""
     import oracle
 
-    threads = int(os.environ.get("NSA_ORACLE_THREADS", "0")) or min(16, os.cpu_count() or 1)
-    T = wl.seq_len
-    n = budget_rows or min(T, 1024)
-    rows = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
-    t0 = time.perf_counter()
-    oracle.forward(arrs_f64["q"], arrs_f64["k"], arrs_f64["v"], arrs_f64["gates"],
-                   top_k=wl.top_k, window=wl.window, scale=wl.scale, rows=rows, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(wl.batch * len(rows) / dt, 2), "unit": "tokens/s", "cores": threads,
+    threads = oracle_threads()
+    passes, t_total = 0, 0.0
+    while passes < max_passes and (passes == 0 or t_total < min_seconds):
+        t0 = time.perf_counter()
+        oracle.forward(arrs_f64["q"], arrs_f64["k"], arrs_f64["v"], arrs_f64["gates"],
+                       top_k=wl.top_k, window=wl.window, scale=wl.scale, threads=threads)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    tokens = wl.batch * wl.seq_len
+    return {"value": round(tokens * passes / t_total, 2), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(rows)} of {T} query positions (evenly spaced) x batch {wl.batch}, "
-                      f"all heads, fp64, {dt:.2f} s"}
+            "sample": f"{passes} full forward pass(es) of {wl.name} (batch {wl.batch} x "
+                      f"{wl.seq_len} positions, all heads, fp64), {t_total:.1f} s total"}
+
+
+# --- HBM traffic of the dominant kernel from committed rocprofv3 counters -----
+PROFILES = os.path.join(ROOT, "profiles")
+K3_SOURCES = ["sparse_attention_long_compress_amd/csrc/sel_win.hip",
+              "sparse_attention_long_compress_amd/csrc/nsa_device.h",
+              "sparse_attention_long_compress_amd/csrc/nsa_launch.h"]
+
+
+def kernel_source_hash(paths=K3_SOURCES):
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_summary(path):
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def committed_traffic(workload):
+    """Bytes per launch of sel_win_kernel from profiles/, or None when the
+    summary is missing or the kernel source changed since it was taken."""
+    summ = read_summary(os.path.join(PROFILES, f"sel_win_kernel_{workload}_traffic.txt"))
+    if not summ or summ.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(summ["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, kernel):
+    """Text summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) for `kernel`,
+    scaled by what the same counters read for a copy kernel of known size."""
+    import csv
+
+    def per_dispatch(path, name_part, counter):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return sum(vals) / len(vals), len(vals)
+
+    def biggest(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        return max(float(r["Counter_Value"]) for r in rows)
+
+    f_kib, nf = per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
+    w_kib, nw = per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    cf = copy_bytes / 1024.0 / biggest(copy_fetch_csv, "FETCH_SIZE")
+    cw = copy_bytes / 1024.0 / biggest(copy_write_csv, "WRITE_SIZE")
+    traffic = (f_kib * cf + w_kib * cw) * 1024.0
+    lines = [f"kernel: {kernel}", f"source_hash: {kernel_source_hash()}",
+             f"fetch_kib_per_dispatch: {f_kib:.1f}  (mean of {nf} dispatches)",
+             f"write_kib_per_dispatch: {w_kib:.1f}  (mean of {nw} dispatches)",
+             f"copy_kernel_bytes: {copy_bytes}",
+             f"copy_fetch_factor: {cf:.4f}", f"copy_write_factor: {cw:.4f}",
+             f"traffic_bytes_per_launch: {traffic:.0f}"]
+    return "\n".join(lines)
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size (one elementwise kernel per call), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = nbytes // 4
+    a = torch.ones(n, device="cuda", dtype=torch.float32)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -88,7 +179,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + steps and exit without the oracle (for rocprofv3)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                       "COPY_WRITE_CSV"),
+                    help="print the traffic summary of sel_win_kernel from rocprofv3 CSVs and exit")
+    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary, copy_bytes=args.copy_bytes, kernel="sel_win_kernel"))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the forward shards over batch or KV groups with no exchange; see DESIGN.md). "
@@ -168,11 +271,13 @@ def main():
                      "sel_win_combine": round(k3 * 1e6, 2), "events_total": round(ev_step * 1e6, 2)},
         "roofline": {"kernel": "sel_win_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": committed_traffic(wl.name)},
     }
     if not args.no_cpu_baseline:
         f64 = {k: as_f64(v) for k, v in cpu.items()}
         res["cpu_baseline"] = cpu_baseline(wl, f64)
+        res["cpu_baseline"]["gpu_over_cpu"] = round(res["value"] / res["cpu_baseline"]["value"], 1)
     print(json.dumps(res), flush=True)
 
 

@@ -16,7 +16,8 @@ Parity-pin status (what pins each function; see tests/test_oracle_pins.py):
   forward/o_cmp     constant keys (uniform weights, closed form), torch fp64
                     SDPA over avg-pooled keys with a block-causal mask
   forward/indices   all-ties closed form, brute-force subset enumeration,
-                    numpy stable argsort, P:53 sparsity arithmetic
+                    numpy stable argsort, the sparsity arithmetic of the
+                    "Sparsity is Cool" Key claims (tests/golden)
   forward/o_sel     full causal attention when top-k covers all blocks (torch
                     SDPA), explicit-mask SDPA given the index table
   forward/o_win     W >= T full causal, W = 1 returns v_t, banded-mask SDPA

@@ -9,10 +9,10 @@
 //   query heads of KV group g; block 0 and the query's own block are always
 //   selected and count toward k; ties go to the lower block index.
 //
-// One workgroup (4 waves) per (tile of P query positions, KV group g, batch b);
+// One workgroup (up to 8 waves) per (tile of P query positions, KV group g, batch b);
 // every position of a tile lies in the same 64-token block c, so they share the
 // candidate set 1..c-1.  Query rows are ordered (position, head), 16 rows form
-// one MFMA column group, each wave owns R/4 rows.  Pooled keys and values are
+// one MFMA column group, each wave owns R/NW rows.  Pooled keys and values are
 // staged in LDS 64 blocks at a time (shared by all waves).
 //   Pass 1: S^T = Kc Q^T on MFMA, online softmax, o_cmp = P Vc, and
 //           U = max_j (tau q.Kc_j + tau |q| radius_j) over blocks 0 .. own, an
@@ -20,9 +20,9 @@
 //           (log2 units).
 //   Pass 2: recompute S^T, p = exp(s - lse), sum p over the G heads of each
 //           position with DPP (adjacent lanes), stage S[position][block] in LDS
-//           64 candidates at a time; each wave scans a quarter of them with one
-//           lane per position keeping a top-m list in registers, and the four
-//           lists are merged at the end.  A candidate is a 32-bit key: the score
+//           64 candidates at a time; each wave scans its share of them with
+//           one lane per position keeping a top-m list in registers, and the
+//           waves' lists are merged at the end.  A candidate is a 32-bit key: the score
 //           in fixed point (21 bits over [0, G], resolution G / 2^21) above the
 //           field 2047 - j, so "higher score, then lower index" is one unsigned
 //           compare and inserting into the sorted list is one v_med3_u32 per
@@ -58,20 +58,24 @@ template <typename T, int D, int G>
 struct K2Cfg {
   static constexpr int P = (256 / G) < 64 ? (256 / G) : 64;  // positions per tile
   static constexpr int R = P * G;                            // rows per tile
-  static constexpr int RWV = R / 4;                          // rows per wave
+  static constexpr int NW = (R / 16) < 8 ? (R / 16) : 8;     // waves (at least one column group each)
+  static constexpr int NT = NW * 64;
+  static constexpr int RWV = R / NW;                         // rows per wave
   static constexpr int CGW = RWV / 16;                       // column groups per wave
+  static constexpr int CPW = 64 / NW;                        // top-k candidates per wave and chunk
   static constexpr int KS = D / 32, MT = D / 16;
   static constexpr int KST = D + 8;   // LDS row stride of the pooled-key chunk
   static constexpr int VST = 64 + 8;  // LDS row stride of the pooled-value chunk
 };
 
 template <typename T, int D, int G, int LMAX>
-__global__ __launch_bounds__(256) void cmp_select_kernel(
+__global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
     Shape s, const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ kcl,
     const T* __restrict__ vct, const float* __restrict__ radius, T* __restrict__ o_cmp,
     float* __restrict__ ubound, int32_t* __restrict__ indices, int do_topk) {
   typedef K2Cfg<T, D, G> C;
   constexpr int P = C::P, CGW = C::CGW, KS = C::KS, MT = C::MT, KST = C::KST, VST = C::VST;
+  constexpr int NW = C::NW, NT = C::NT, CPW = C::CPW;
   typedef typename Frag<T>::type FragT;
   constexpr int EPV = 16 / sizeof(T);
 
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
   __shared__ __align__(16) T Ls[64 * KST];
   __shared__ __align__(16) T Vs[D * VST];
   __shared__ float S_l[P][65];
-  __shared__ uint32_t mlist[3][P][LMAX];
+  __shared__ uint32_t mlist[NW - 1][P][LMAX];
 
   const int NTL = s.T / P;
   int bg, tile;
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
   // stage pooled keys (and the residual) of blocks jb .. jb+63, and optionally
   // the pooled values; rows past the last complete block are clamped (masked)
   auto stage = [&](int jb, bool with_v) {
-    for (int i = threadIdx.x; i < 64 * (D / EPV); i += 256) {
+    for (int i = threadIdx.x; i < 64 * (D / EPV); i += NT) {
       const int r = i / (D / EPV), c8 = i % (D / EPV);
       const int key = min(jb + r, s.nc - 1);
       *reinterpret_cast<int4*>(Ks + r * KST + c8 * EPV) =
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
             *reinterpret_cast<const int4*>(kcl_b + (size_t)key * kc_row + c8 * EPV);
     }
     if (with_v)
-      for (int i = threadIdx.x; i < D * (64 / EPV); i += 256) {
+      for (int i = threadIdx.x; i < D * (64 / EPV); i += NT) {
         const int r = i / (64 / EPV), c8 = i % (64 / EPV);
         *reinterpret_cast<int4*>(Vs + r * VST + c8 * EPV) =
             *reinterpret_cast<const int4*>(vct_b + (size_t)r * s.ncp + jb + c8 * EPV);
@@ -258,13 +262,13 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
         }
       }
       __syncthreads();
-      // wave w scans candidates jb + 16w .. jb + 16w + 15, one lane per position
+      // wave w scans candidates jb + CPW w .. jb + CPW (w + 1) - 1, one lane per position
       if (l < P) {
-        const int j0 = jb + 16 * w, j1 = min(jb + 16 * w + 16, c);
+        const int j0 = jb + CPW * w, j1 = min(jb + CPW * w + CPW, c);
         for (int jj = j0; jj < j1; ++jj) insert_desc(list, topk_key(S_l[l][jj - jb], qscale, jj));
       }
     }
-    // merge the four per-wave lists into wave 0's
+    // merge the per-wave lists into wave 0's
     __syncthreads();
     if (w > 0 && l < P) {
 #pragma unroll
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256) void cmp_select_kernel(
       // a rolled loop: fully unrolled chains of med3 insertions make the
       // compiler's min/max combining blow up
 #pragma nounroll
-      for (int vi = 0; vi < 3 * LMAX; ++vi) insert_desc(list, mlist[vi / LMAX][l][vi % LMAX]);
+      for (int vi = 0; vi < (NW - 1) * LMAX; ++vi) insert_desc(list, mlist[vi / LMAX][l][vi % LMAX]);
     }
   }
 
@@ -312,14 +316,14 @@ template <typename T, int D, int G>
 static hipError_t launch_cs(const Shape& s, const void* q, const void* kc, const void* kcl,
                             const void* vct, const float* radius, void* o_cmp, float* ubound,
                             int32_t* indices, bool do_topk, hipStream_t st) {
-  constexpr int P = K2Cfg<T, D, G>::P;
+  constexpr int P = K2Cfg<T, D, G>::P, NT = K2Cfg<T, D, G>::NT;
   dim3 grid(s.T / P * s.Hkv * s.B);
   if (s.topk - 2 <= 16)
-    hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 16>), grid, dim3(256), 0, st, s, (const T*)q,
+    hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 16>), grid, dim3(NT), 0, st, s, (const T*)q,
                        (const T*)kc, (const T*)kcl, (const T*)vct, radius, (T*)o_cmp, ubound,
                        indices, do_topk ? 1 : 0);
   else
-    hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 32>), grid, dim3(256), 0, st, s, (const T*)q,
+    hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 32>), grid, dim3(NT), 0, st, s, (const T*)q,
                        (const T*)kc, (const T*)kcl, (const T*)vct, radius, (T*)o_cmp, ubound,
                        indices, do_topk ? 1 : 0);
   return hipGetLastError();

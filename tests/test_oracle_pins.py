@@ -217,7 +217,7 @@ def test_sparsity_arithmetic_from_the_pages():
     # ~81% sparsity as MoBA 512 / top-3: 1 - (16*64 + 512)/8192 = 0.8125.  This
     # holds only if k counts the forced blocks: the last query attends exactly 16
     # blocks of 64 plus a 512-token window.
-    fx = json.load(open(os.path.join(GOLDEN, "sparsity_p53.json")))
+    fx = json.load(open(os.path.join(GOLDEN, "sparsity_nsa_vs_moba.json")))
     T, blk, topk, W = fx["seq_len"], fx["block"], fx["top_k"], fx["window"]
     q, k, v, g = rand_inputs(1, T, 1, 1, 2, seed=12)
     r = oracle.forward(q, k, v, g, top_k=topk, window=W)
