@@ -148,9 +148,11 @@ __device__ __forceinline__ float xsum4(float v) {
 
 // Staged image of one 64-key block of one KV group, the unit the selection /
 // window kernel copies global -> LDS.  It is the block's K and V^T as MFMA
-// fragments, K fragments first: fragment f < NFRAG is K subtile u = f / KS
-// (16 keys) at k step ks = f % KS; fragment NFRAG + 2 mt + h is V^T channel
-// tile mt (16 channels) over keys 32 h .. 32 h + 31.  A fragment is NV pieces
+// fragments, K fragments first: fragment f < NFRAG is K subtile u = f % 4
+// (16 keys) at k step ks = f / 4; fragment NFRAG + h (D / 16) + mt is V^T
+// channel tile mt (16 channels) over keys 32 h .. 32 h + 31.  Consecutive
+// fragments therefore feed different accumulators (no dependent MFMA pairs
+// inside a batch of fragments).  A fragment is NV pieces
 // of 64 lanes x 16 bytes (lane l holds its 8 elements; fp32 needs two
 // pieces), so every piece is one contiguous 1 KB copy.  Inside a 32-key half,
 // MFMA row rho of K subtile u holds key 8 (rho / 4) + 4 (u % 2) + rho % 4: the
@@ -162,6 +164,11 @@ struct KvImage {
   static constexpr int EPV = 16 / (int)sizeof(T);      // elements per piece and lane
   static constexpr int KS = D / 32;
   static constexpr int NFRAG = D / 8;                  // fragments per operand (4 KS = 2 (D/16))
+  static constexpr int MT = D / 16;                    // 16-channel tiles of V^T
+  static __device__ __forceinline__ int k_u(int f) { return f & 3; }     // K fragment -> subtile
+  static __device__ __forceinline__ int k_ks(int f) { return f >> 2; }   // K fragment -> k step
+  static __device__ __forceinline__ int v_mt(int f2) { return f2 % MT; } // V fragment -> channel tile
+  static __device__ __forceinline__ int v_h(int f2) { return f2 / MT; }  // V fragment -> key half
   static constexpr int PIECES = 2 * NFRAG * NV;
   static constexpr int BYTES = PIECES * 1024;
   // key (0..63 within the block) in K fragment row rho (= lane % 16) of subtile u

@@ -138,10 +138,10 @@ __global__ __launch_bounds__(256) void pool_kernel(Shape s, const T* __restrict_
       const int a = l / 16, rho = l % 16;
       const T* src;
       if (f < I::NFRAG) {
-        const int u = f / I::KS, ks = f % I::KS;
+        const int u = I::k_u(f), ks = I::k_ks(f);
         src = &ktile[I::krow(u, rho)][ks * 32 + 8 * a + vv * I::EPV];
       } else {
-        const int f2 = f - I::NFRAG, mt = f2 / 2, hf = f2 % 2;
+        const int f2 = f - I::NFRAG, mt = I::v_mt(f2), hf = I::v_h(f2);
         src = &tr[mt * 16 + rho][32 * hf + 8 * a + vv * I::EPV];
       }
       T piece[I::EPV];

@@ -200,6 +200,7 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
   constexpr int KS = C::KS, MT = C::MT, NV = C::NV, EPV = C::EPV, NFRAG = C::NFRAG, FCH = C::FCH;
   constexpr int FRAG_BYTES = C::FRAG_BYTES, STAGE = C::STAGE, NBUF = C::NBUF, GB = C::GB, LOADS = C::LOADS;
   typedef typename Frag<T>::type FragT;
+  typedef typename C::Img Img;
   const float INF = __builtin_inff();
 
   const T* __restrict__ q = (const T*)args.q;
@@ -462,7 +463,7 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
         if (!act[cg]) continue;
 #pragma unroll
         for (int i = 0; i < FCH; ++i) {
-          const int u = (f0 + i) / KS, ks = (f0 + i) % KS;
+          const int u = Img::k_u(f0 + i), ks = Img::k_ks(f0 + i);
           st[cg][u] = mma(st[cg][u], kf[i], qf[cg][ks]);
         }
       }
@@ -547,14 +548,14 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
         if (act_s[cg]) {
 #pragma unroll
           for (int i = 0; i < FCH; ++i) {
-            const int mt = (f0 + i) / 2, hf = (f0 + i) % 2;
+            const int mt = Img::v_mt(f0 + i), hf = Img::v_h(f0 + i);
             acc_s[cg][mt] = mma(acc_s[cg][mt], vf[i], ps[cg][hf]);
           }
         }
         if (act_w[cg]) {
 #pragma unroll
           for (int i = 0; i < FCH; ++i) {
-            const int mt = (f0 + i) / 2, hf = (f0 + i) % 2;
+            const int mt = Img::v_mt(f0 + i), hf = Img::v_h(f0 + i);
             acc_w[cg][mt] = mma(acc_w[cg][mt], vf[i], pw[cg][hf]);
           }
         }
