@@ -5,8 +5,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one whole forward pass (pool, compressed attention + top-k,
 selection + window + gated combine) over one batch of seeded synthetic input
-already resident in HBM.  Prints ONE JSON line (rank 0, N = 1):
-  value      = tokens/s = batch * seq_len / (seconds per step)
+already resident in HBM; the selection-branch backward of the same input (the
+rest of the hot path) is timed after it and reported beside the forward.
+Prints ONE JSON line (rank 0, N = 1):
+  value      = forward tokens/s = batch * seq_len / (seconds per forward step)
   roofline   = the selection/window/combine kernel (the dominant one): useful
                attention FLOPs per launch / its average duration, measured with
                HIP events recorded around it on its own stream in every timed
@@ -50,6 +52,14 @@ def useful_flops(wl):
     sel, win, cmp = useful_counts(wl)
     per = 4 * wl.head_dim * wl.batch * wl.n_q_heads
     return {"sel_win": per * (sel + win), "cmp": per * cmp, "total": per * (sel + win + cmp)}
+
+
+def useful_bwd_flops(wl):
+    """Selection-branch backward: 10 D FLOPs per (query, head, selected key s <= t)
+    (dP = dO V^T, dV += P^T dO, dQ += dS K, dK += dS^T Q, 2 D each, plus the
+    recomputed S = Q K^T)."""
+    sel, _, _ = useful_counts(wl)
+    return 10 * wl.head_dim * wl.batch * wl.n_q_heads * sel
 
 
 def algorithmic_bytes(wl):
@@ -185,6 +195,8 @@ def main():
                                                        "COPY_WRITE_CSV"),
                     help="print the traffic summary of sel_win_kernel from rocprofv3 CSVs and exit")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    ap.add_argument("--no-backward", action="store_true",
+                    help="time the forward only (the selection-branch backward is timed by default)")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary, copy_bytes=args.copy_bytes, kernel="sel_win_kernel"))
@@ -205,7 +217,7 @@ def main():
     from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64, draw, to_dtype
 
     wl = WORKLOADS[args.workload]
-    arrs = draw(wl)
+    arrs = draw(wl, with_dout=not args.no_backward)
     cpu = to_dtype(arrs, wl.dtype)
     dev = {k: v.to("cuda") for k, v in cpu.items()}
     del arrs
@@ -236,6 +248,33 @@ def main():
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
 
+    # the rest of the hot path: the selection-branch backward of the same
+    # input, fed by the forward's saved indices, log-sum-exp and o_sel
+    bwd = None
+    if not args.no_backward:
+        res_f = nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                            window=wl.window, scale=wl.scale, workspace=ws, want_indices=True,
+                            want_lse=True, want_o_sel=True)
+        wsb = nsa.alloc_workspace(p, dev["q"].device, backward=True)
+        grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]))
+
+        def bstep():
+            nsa.select_bwd(dev["q"], dev["k"], dev["v"], dev["gates"], res_f["indices"],
+                           res_f["lse_sel"], res_f["o_sel"], dev["dout"], top_k=wl.top_k,
+                           scale=wl.scale, workspace=wsb, out=grads)
+
+        for _ in range(args.warmup):
+            bstep()
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in bev:
+            e0.record()
+            bstep()
+            e1.record()
+        torch.cuda.synchronize()
+        bwd = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])) * 1e-3
+
     k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
     k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
     k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
@@ -244,7 +283,8 @@ def main():
     tokens = wl.batch * wl.seq_len
     if args.profile_only:
         print(json.dumps({"profile_only": True, "ms_per_step": wall * 1e3,
-                          "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6}), flush=True)
+                          "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6,
+                          "sel_bwd_us": None if bwd is None else bwd * 1e6}), flush=True)
         return
 
     achieved = fl["sel_win"] / k3 / 1e12
@@ -274,6 +314,13 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic(wl.name)},
     }
+    if bwd is not None:
+        fb = useful_bwd_flops(wl)
+        res["selection_backward"] = {
+            "us": round(bwd * 1e6, 2), "useful_tflops": round(fb / bwd / 1e12, 2),
+            "pct_bf16_peak": round(100 * fb / bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "fwd_plus_bwd_ms": round((wall + bwd) * 1e3, 4),
+            "fwd_plus_bwd_tokens_per_s": round(tokens / (wall + bwd), 1)}
     if not args.no_cpu_baseline:
         f64 = {k: as_f64(v) for k, v in cpu.items()}
         res["cpu_baseline"] = cpu_baseline(wl, f64)

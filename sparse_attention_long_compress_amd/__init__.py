@@ -200,14 +200,18 @@ def forward(q, k, v, gates, *, top_k, window, scale=None, flags=0, indices=None,
 
 
 def select_bwd(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, scale=None,
-               workspace=None, stream=None):
-    """(dq, dk, dv) of the selection branch (nsa_select_bwd)."""
+               workspace=None, stream=None, out=None):
+    """(dq, dk, dv) of the selection branch (nsa_select_bwd); `out` may pass
+    preallocated (dq, dk, dv)."""
     torch = _torch()
     p = params_for(q, k, top_k=top_k, window=1, scale=scale)
     ws = workspace if workspace is not None else alloc_workspace(p, q.device, backward=True)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    if out is not None:
+        dq, dk, dv = out
+    else:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
     _check(lib().nsa_select_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(indices),
                                 _ptr(lse_sel), _ptr(o_sel), _ptr(dout), ctypes.byref(p), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
