@@ -73,13 +73,13 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
 
 // Backward workspace regions.
 struct BwdLayout {
-  size_t kt, delta, dos, revmap, items, slots, part, total;
+  size_t bimg, delta, dos, revmap, items, slots, part, total;
 };
 BwdLayout bwd_layout(const Shape& s, size_t es) {
   BwdLayout L;
   size_t o = 0;
   const size_t nblk = s.T / 64;
-  L.kt = o;     o += up((size_t)s.B * s.Hkv * s.D * s.T * es, kAlign);
+  L.bimg = o;   o += up((size_t)s.B * s.Hkv * nblk * 3 * 64 * s.D * es, kAlign);
   L.delta = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
   L.dos = o;    o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
   L.revmap = o; o += up((size_t)s.B * s.Hkv * nblk * nblk * 8, kAlign);
@@ -237,12 +237,12 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   char* ws = (char*)workspace;
   const bool bf = p->dtype == NSA_BF16;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = nsa::launch_bwd_prep(bf, s, k, gates, o_sel, dout, ws + L.kt,
+  hipError_t e = nsa::launch_bwd_prep(bf, s, k, v, gates, o_sel, dout, ws + L.bimg,
                                       (float*)(ws + L.delta), ws + L.dos, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_revmap(s, indices, (uint64_t*)(ws + L.revmap), hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_dq(bf, s, q, k, ws + L.kt, v, indices, lse_sel, (const float*)(ws + L.delta),
+  e = nsa::launch_bwd_dq(bf, s, q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta),
                          ws + L.dos, dq, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_dkdv(bf, s, q, k, v, lse_sel, (const float*)(ws + L.delta), ws + L.dos,

@@ -10,13 +10,13 @@
 // Delta = dOs . o_sel and dS_s = P_s (dP_s - Delta):
 //   dq = tau sum_s dS_s k_s,   dk_s = tau sum dS_s q,   dv_s = sum P_s dOs.
 //
-// B0 prep    : dOs = g_sel dO (element type), Delta (fp32), K^T copy.
+// B0 prep    : dOs = g_sel dO (element type), Delta (fp32), block images
+//              (K, V, K^T fragments) for B2.
 // B1 revmap  : M[b][g][j][c] = 64-bit mask of the positions of tile c (64
 //              positions) that selected block j -- one wave per (tile, group),
 //              one lane per position, a ballot per block; no atomics.
-// B2 dq      : query-stationary, the walk of the forward's selection kernel
-//              (K, K^T, V of a block staged in LDS, lane-slot packed 16-row
-//              MFMA tiles, register accumulators).
+// B2 dq      : query-stationary, the block walk of the forward's selection
+//              kernel (bwd_dq.hip).
 // B3 dk/dv   : key/value-stationary: a workgroup owns one key block (each wave
 //              16 keys, accumulators in registers) and a range of query tiles;
 //              the rows that selected the block (from M) are compacted into
@@ -36,26 +36,53 @@ template <> struct V16b<bf16> { typedef bf16x8 type; };
 template <> struct V16b<float> { typedef f32x4 type; };
 
 // ============================================================ B0: preparation
-// grid (nblk, Hkv, B), 256 threads: block j of positions, KV group g.
+// grid (nblk, Hkv, B), 256 threads: block j of positions / keys, KV group g.
+// Writes the block's backward image (K, V, K^T fragments, BwdImage) and, for
+// the G heads of the group at these positions, dOs = g_sel dO and Delta.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restrict__ k,
+                                                       const T* __restrict__ v,
                                                        const T* __restrict__ gates,
                                                        const T* __restrict__ o_sel,
                                                        const T* __restrict__ dout,
-                                                       T* __restrict__ kt, float* __restrict__ delta,
+                                                       unsigned char* __restrict__ bimg,
+                                                       float* __restrict__ delta,
                                                        T* __restrict__ dos) {
-  __shared__ T tr[D][kBlock + 8];
+  typedef BwdImage<T, D> I;
+  constexpr int EPV = 16 / sizeof(T);
+  typedef typename V16b<T>::type Vec;
+  __shared__ __align__(16) T kt[kBlock][D + 8];
+  __shared__ __align__(16) T vt[kBlock][D + 8];
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = s.G;
-  // K^T of the block (positions 64j .. 64j+63, head g)
-  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
-    const int r = i / D, d = i % D;
-    tr[d][r] = k[(((size_t)b * s.T + j * kBlock + r) * s.Hkv + g) * D + d];
+  const size_t k_row = (size_t)s.Hkv * D;
+  for (int i = threadIdx.x; i < kBlock * (D / EPV); i += 256) {
+    const int r = i / (D / EPV), c8 = i % (D / EPV);
+    const size_t src = ((size_t)b * s.T + j * kBlock + r) * k_row + (size_t)g * D + c8 * EPV;
+    *reinterpret_cast<Vec*>(&kt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(k + src);
+    *reinterpret_cast<Vec*>(&vt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(v + src);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
-    const int d = i / kBlock, r = i % kBlock;
-    kt[(((size_t)b * s.Hkv + g) * D + d) * s.T + j * kBlock + r] = tr[d][r];
+  unsigned char* img = bimg + (((size_t)b * s.Hkv + g) * (s.T / kBlock) + j) * (size_t)I::BYTES;
+  for (int w = threadIdx.x; w < I::PIECES * 64; w += 256) {
+    const int pc = w / 64, l = w % 64;
+    const int f = pc / I::NV, vv = pc % I::NV;
+    const int a = l / 16, rho = l % 16;
+    T piece[EPV];
+    if (f < 2 * I::NFRAG) {  // K or V, key rows
+      const int ff = f % I::NFRAG;
+      const int u = I::K::k_u(ff), ks = I::K::k_ks(ff);
+      const T* src = (f < I::NFRAG ? &kt[0][0] : &vt[0][0]) +
+                     (size_t)I::K::krow(u, rho) * (D + 8) + ks * 32 + 8 * a + vv * EPV;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) piece[e] = src[e];
+    } else {                 // K^T: channel rows, 8 consecutive keys per lane
+      const int f2 = f - 2 * I::NFRAG, mt = I::K::v_mt(f2), hf = I::K::v_h(f2);
+      const int ch = mt * 16 + rho, key0 = 32 * hf + 8 * a + vv * EPV;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) piece[e] = kt[key0 + e][ch];
+    }
+    *reinterpret_cast<f32x4*>(img + (size_t)pc * 1024 + 16 * l) = *reinterpret_cast<const f32x4*>(piece);
   }
   // dOs and Delta for the G heads of the group: one wave per (position, head) row
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
@@ -65,9 +92,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
     const float gs = (float)gates[(((size_t)b * s.T + t) * s.Hq + h) * 3 + 1];
     float acc = 0.f;
     for (int d = l; d < D; d += kWave) {
-      const float v = gs * (float)dout[base + d];
-      dos[base + d] = (T)v;
-      acc += v * (float)o_sel[base + d];
+      const float v_ = gs * (float)dout[base + d];
+      dos[base + d] = (T)v_;
+      acc += v_ * (float)o_sel[base + d];
     }
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (l == 0) delta[((size_t)b * s.Hq + h) * s.T + t] = acc;
@@ -95,189 +122,6 @@ __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* 
   for (int j = 0; j <= c; ++j) {
     const uint64_t m = __builtin_amdgcn_ballot_w64(bits[j * 64 + l] != 0);
     if (l == 0) dst[(size_t)j * nblk + c] = m;
-  }
-}
-
-// ============================================================ B2: dq
-template <typename T, int D, int G>
-struct DqCfg {
-  static constexpr int NW = 4;
-  static constexpr int NT = NW * 64;
-  static constexpr int RWT = (D == 128 || sizeof(T) == 4) ? 32 : 64;
-  static constexpr int P = (NW * RWT / G) < 64 ? (NW * RWT / G) : 64;
-  static constexpr int R = P * G;
-  static constexpr int RW = R / NW;
-  static constexpr int NCG = RW / 16;
-  static constexpr int NSG = 16 / G;
-  static constexpr int PW = RW / G;
-  static constexpr int KS = D / 32, MT = D / 16;
-  static constexpr int QST = D + 8, VST = 64 + 8;
-  static_assert(RW % 16 == 0, "rows per wave");
-};
-
-template <typename T, int D, int G>
-static size_t dq_lds_bytes(int topk) {
-  typedef DqCfg<T, D, G> C;
-  return sizeof(T) * ((size_t)2 * 64 * C::QST + (size_t)D * C::VST + (size_t)2 * C::R * C::QST) +
-         (size_t)C::P * topk * 2 + 16;
-}
-
-template <typename T, int D, int G>
-__global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
-    Shape s, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ kt,
-    const T* __restrict__ v, const int32_t* __restrict__ indices, const float* __restrict__ lse,
-    const float* __restrict__ delta, const T* __restrict__ dos, T* __restrict__ dq) {
-  typedef DqCfg<T, D, G> C;
-  constexpr int NT = C::NT, P = C::P, R = C::R, NCG = C::NCG, NSG = C::NSG, PW = C::PW;
-  constexpr int KS = C::KS, MT = C::MT, QST = C::QST, VST = C::VST;
-  typedef typename Frag<T>::type FragT;
-  typedef typename V16b<T>::type Vec;
-  constexpr int EPV = 16 / sizeof(T);
-
-  const int NTL = s.T / P;
-  int bg, tile;
-  xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
-  const int g = bg % s.Hkv, b = bg / s.Hkv;
-  const int t0 = tile * P;
-  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  const int a = l / 16, col = l % 16;
-  const int sg = col / G, hh = col % G;
-  const float c1 = s.scale * kLog2e;
-  const int topk = s.topk;
-  const size_t k_row = (size_t)s.Hkv * D, q_row = (size_t)s.Hq * D;
-  const T* k_b = k + (size_t)b * s.T * k_row + (size_t)g * D;
-  const T* v_b = v + (size_t)b * s.T * k_row + (size_t)g * D;
-  const T* kt_b = kt + ((size_t)b * s.Hkv + g) * (size_t)D * s.T;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Kl = reinterpret_cast<T*>(smem);  // [64][QST]
-  T* Vl = Kl + 64 * QST;               // [64][QST]
-  T* Ktl = Vl + 64 * QST;              // [D][VST]
-  T* Ql = Ktl + D * VST;               // [R][QST]
-  T* Dl = Ql + (size_t)R * QST;        // [R][QST]
-  int16_t* lists = reinterpret_cast<int16_t*>(Dl + (size_t)R * QST);
-
-  for (int i = threadIdx.x; i < R * (D / EPV); i += NT) {
-    const int r = i / (D / EPV), c8 = i % (D / EPV);
-    const int p = r / G, h2 = r % G;
-    const size_t src = ((size_t)b * s.T + t0 + p) * q_row + (size_t)(g * G + h2) * D + c8 * EPV;
-    *reinterpret_cast<Vec*>(Ql + (size_t)r * QST + c8 * EPV) = *reinterpret_cast<const Vec*>(q + src);
-    *reinterpret_cast<Vec*>(Dl + (size_t)r * QST + c8 * EPV) = *reinterpret_cast<const Vec*>(dos + src);
-  }
-  for (int i = threadIdx.x; i < P * topk; i += NT) {
-    const int p = i / topk, e = i % topk;
-    const int j = indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e];
-    lists[i] = (int16_t)(j < 0 ? 0x7fff : j);
-  }
-  __syncthreads();
-
-  float lse2[NCG], dl[NCG];
-  int ptr[NCG], nxt[NCG];
-  f32x4 acc[NCG][MT];
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int p = w * PW + cg * NSG + sg;
-    const int t = t0 + p, h = g * G + hh;
-    lse2[cg] = lse[((size_t)b * s.Hq + h) * s.T + t] * kLog2e;
-    dl[cg] = delta[((size_t)b * s.Hq + h) * s.T + t];
-    ptr[cg] = 0;
-    nxt[cg] = lists[p * topk];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[cg][mt] = zero4();
-  }
-
-  const int c_last = (t0 + P - 1) / kBlock;
-  for (int j = 0; j <= c_last; ++j) {
-    // stage K, V (row-major) and K^T of block j
-    for (int i = threadIdx.x; i < 64 * (D / EPV); i += NT) {
-      const int r = i / (D / EPV), c8 = i % (D / EPV);
-      *reinterpret_cast<Vec*>(Kl + r * QST + c8 * EPV) =
-          *reinterpret_cast<const Vec*>(k_b + (size_t)(j * kBlock + r) * k_row + c8 * EPV);
-      *reinterpret_cast<Vec*>(Vl + r * QST + c8 * EPV) =
-          *reinterpret_cast<const Vec*>(v_b + (size_t)(j * kBlock + r) * k_row + c8 * EPV);
-    }
-    for (int i = threadIdx.x; i < D * (64 / EPV); i += NT) {
-      const int r = i / (64 / EPV), c8 = i % (64 / EPV);
-      *reinterpret_cast<Vec*>(Ktl + r * VST + c8 * EPV) =
-          *reinterpret_cast<const Vec*>(kt_b + (size_t)r * s.T + j * kBlock + c8 * EPV);
-    }
-    __syncthreads();
-
-    int gm = 0;
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      if (nxt[cg] == j) {
-        gm |= 1 << cg;
-        ++ptr[cg];
-        const int p = w * PW + cg * NSG + sg;
-        nxt[cg] = ptr[cg] < topk ? lists[p * topk + ptr[cg]] : 0x7fff;
-      }
-    }
-    const int cnt = __popc(gm);
-    for (int tt = 0; __builtin_amdgcn_ballot_w64(tt < cnt) != 0; ++tt) {
-      int rem = gm;
-      for (int z = 0; z < tt; ++z) rem &= rem - 1;
-      const int cgt = rem ? __ffs(rem) - 1 : 0;
-      const bool valid = tt < cnt;
-      const int p = w * PW + cgt * NSG + sg;
-      const int t = t0 + p;
-      const int row = p * G + hh;
-      float lr = lse2[0], dr = dl[0];
-#pragma unroll
-      for (int cg = 1; cg < NCG; ++cg) {
-        lr = cg == cgt ? lse2[cg] : lr;
-        dr = cg == cgt ? dl[cg] : dr;
-      }
-      FragT qf[KS], df[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = Frag<T>::load(Ql + (size_t)row * QST + ks * 32 + a * 8);
-        df[ks] = Frag<T>::load(Dl + (size_t)row * QST + ks * 32 + a * 8);
-      }
-      float ds[2][8];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int kr = cc * 32 + 8 * (col / 4) + 4 * u + (col % 4);
-          f32x4 st = zero4(), dp = zero4();
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            st = mma(st, Frag<T>::load(Kl + (size_t)kr * QST + ks * 32 + a * 8), qf[ks]);
-            dp = mma(dp, Frag<T>::load(Vl + (size_t)kr * QST + ks * 32 + a * 8), df[ks]);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = j * kBlock + cc * 32 + 8 * a + 4 * u + r;
-            const float pr = (valid && key <= t) ? fast_exp2(st[r] * c1 - lr) : 0.f;
-            ds[cc][4 * u + r] = pr * (dp[r] - dr);
-          }
-        }
-      const FragT sf0 = Frag<T>::from_f32(ds[0]);
-      const FragT sf1 = Frag<T>::from_f32(ds[1]);
-      float msk[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) msk[cg] = (valid && cg == cgt) ? 1.f : 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const T* krow = Ktl + (size_t)(mt * 16 + col) * VST + 8 * a;
-        f32x4 o = zero4();
-        o = mma(o, Frag<T>::load(krow), sf0);
-        o = mma(o, Frag<T>::load(krow + 32), sf1);
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) acc[cg][mt] += o * msk[cg];
-      }
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int p = w * PW + cg * NSG + sg;
-    const int t = t0 + p, h = g * G + hh;
-    T* dst = dq + ((size_t)b * s.T + t) * q_row + (size_t)h * D;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) store4(dst + mt * 16 + 4 * a, acc[cg][mt] * s.scale);
   }
 }
 
@@ -522,23 +366,24 @@ int bwd_slot_count(int nblk) {
   return n;
 }
 
-hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* gates,
-                           const void* o_sel, const void* dout, void* kt, float* delta, void* dos,
-                           hipStream_t st) {
+hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* v,
+                           const void* gates, const void* o_sel, const void* dout, void* bimg,
+                           float* delta, void* dos, hipStream_t st) {
   dim3 grid(s.T / kBlock, s.Hkv, s.B);
+  unsigned char* im = (unsigned char*)bimg;
   if (is_bf16) {
     if (s.D == 64)
       hipLaunchKernelGGL((bwd_prep_kernel<bf16, 64>), grid, dim3(256), 0, st, s, (const bf16*)k,
-                         (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout, (bf16*)kt, delta,
-                         (bf16*)dos);
+                         (const bf16*)v, (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout,
+                         im, delta, (bf16*)dos);
     else
       hipLaunchKernelGGL((bwd_prep_kernel<bf16, 128>), grid, dim3(256), 0, st, s, (const bf16*)k,
-                         (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout, (bf16*)kt, delta,
-                         (bf16*)dos);
+                         (const bf16*)v, (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout,
+                         im, delta, (bf16*)dos);
   } else {
     hipLaunchKernelGGL((bwd_prep_kernel<float, 64>), grid, dim3(256), 0, st, s, (const float*)k,
-                       (const float*)gates, (const float*)o_sel, (const float*)dout, (float*)kt,
-                       delta, (float*)dos);
+                       (const float*)v, (const float*)gates, (const float*)o_sel,
+                       (const float*)dout, im, delta, (float*)dos);
   }
   return hipGetLastError();
 }
@@ -549,45 +394,6 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
   dim3 grid(nblk, s.Hkv, s.B);
   hipLaunchKernelGGL(bwd_revmap_kernel, grid, dim3(64), (size_t)nblk * 64, st, s, indices, revmap);
   return hipGetLastError();
-}
-
-template <typename T, int D, int G>
-static hipError_t launch_dq_t(const Shape& s, const void* q, const void* k, const void* kt,
-                              const void* v, const int32_t* idx, const float* lse,
-                              const float* delta, const void* dos, void* dq, hipStream_t st) {
-  typedef DqCfg<T, D, G> C;
-  const size_t lds = dq_lds_bytes<T, D, G>(s.topk);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid(s.T / C::P * s.Hkv * s.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, G>), grid, dim3(C::NT), lds, st, s, (const T*)q,
-                     (const T*)k, (const T*)kt, (const T*)v, idx, lse, delta, (const T*)dos,
-                     (T*)dq);
-  return hipGetLastError();
-}
-template <typename T, int D>
-static hipError_t launch_dq_g(const Shape& s, const void* q, const void* k, const void* kt,
-                              const void* v, const int32_t* idx, const float* lse,
-                              const float* delta, const void* dos, void* dq, hipStream_t st) {
-  switch (s.G) {
-    case 1: return launch_dq_t<T, D, 1>(s, q, k, kt, v, idx, lse, delta, dos, dq, st);
-    case 2: return launch_dq_t<T, D, 2>(s, q, k, kt, v, idx, lse, delta, dos, dq, st);
-    case 4: return launch_dq_t<T, D, 4>(s, q, k, kt, v, idx, lse, delta, dos, dq, st);
-    case 8: return launch_dq_t<T, D, 8>(s, q, k, kt, v, idx, lse, delta, dos, dq, st);
-    default: return launch_dq_t<T, D, 16>(s, q, k, kt, v, idx, lse, delta, dos, dq, st);
-  }
-}
-hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* k, const void* kt,
-                         const void* v, const int32_t* indices, const float* lse,
-                         const float* delta, const void* dos, void* dq, hipStream_t st) {
-  if (is_bf16) {
-    if (s.D == 64) return launch_dq_g<bf16, 64>(s, q, k, kt, v, indices, lse, delta, dos, dq, st);
-    return launch_dq_g<bf16, 128>(s, q, k, kt, v, indices, lse, delta, dos, dq, st);
-  }
-  return launch_dq_g<float, 64>(s, q, k, kt, v, indices, lse, delta, dos, dq, st);
 }
 
 template <typename T, int D, int G>

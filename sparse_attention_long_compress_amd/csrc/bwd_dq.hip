@@ -1,0 +1,278 @@
+// bwd_dq.hip -- B2: dq of the selection branch, query-stationary.
+//
+// [SIC] "Sparsity is Cool", Method (NSA implementation): the selection-branch
+// backward as two passes -- this query-stationary pass computes dq, the
+// key/value-stationary pass (bwd.hip) dk and dv, so neither needs atomics.
+// With P_s = exp(tau q.k_s - lse) (the forward's log-sum-exp), dP_s = dOs.v_s,
+// Delta = dOs.o_sel and dS_s = P_s (dP_s - Delta):  dq = tau sum_s dS_s k_s
+// over the keys s <= t of the blocks the row's position selected.
+//
+// The walk is the one of the forward's selection / window kernel: one
+// workgroup per (tile of P positions, KV group g, batch b); each wave owns one
+// 16-row column group (16/G positions x G heads) with its q and dOs fragments
+// and its dq accumulator (MFMA C layout of dq^T: lane = row) in registers.
+// Key blocks 0 .. own(last position) are walked once; each block's backward
+// image (K, V and K^T fragments, written by the preparation kernel) is copied
+// global -> LDS by global_load_lds into a ring of two groups of blocks (one
+// barrier per group).  Per block and column group that attends it (scalar
+// test on the next selected block of its rows):
+//   S^T = K Q^T, dP^T = V dOs^T          (16-key subtiles, key order of the
+//                                          image: C layout = B layout of dS^T)
+//   P = exp2(tau log2(e) s - lse2),       rows that did not select the block
+//                                          get lse2 = +inf (P = 0)
+//   dS = P (dP - Delta) -> bf16,  dq^T += K^T dS^T.
+// Deterministic (no atomics).
+#include <math.h>
+
+#include "nsa_device.h"
+#include "nsa_launch.h"
+
+#ifndef NSA_DQ_RING_BYTES
+#define NSA_DQ_RING_BYTES (144 * 1024)
+#endif
+
+namespace nsa {
+
+template <typename T, int D, int G>
+struct DqCfg {
+  typedef BwdImage<T, D> Img;
+  static constexpr bool WIDE = D == 128 || sizeof(T) == 4;
+  static constexpr int NW = WIDE ? 12 : 16;       // waves per workgroup (one column group each)
+  static constexpr int NT = NW * 64;
+  static constexpr int NSG = 16 / G;              // positions per column group
+  static constexpr int P = NW * NSG;              // positions per workgroup
+  static constexpr int KS = D / 32, MT = D / 16;
+  static constexpr int NV = Img::NV, NFRAG = Img::NFRAG;
+  static constexpr int FCH = (NFRAG < 2 ? NFRAG : 2) / NV > 0 ? (NFRAG < 2 ? NFRAG : 2) / NV : 1;
+  static constexpr int FRAG_BYTES = NV * 1024;
+  static constexpr int STAGE = Img::BYTES;
+  static constexpr int GB = (NSA_DQ_RING_BYTES / STAGE / 2) < 4 ? (NSA_DQ_RING_BYTES / STAGE / 2) : 4;
+  static constexpr int NBUF = 2 * GB;
+  static constexpr int LOADS = Img::PIECES;
+  static_assert(GB >= 1, "ring too small");
+  static_assert(NSG * G == 16, "column group = 16 rows");
+};
+
+template <typename T, int D, int G>
+static size_t dq_lds_bytes(int topk) {
+  typedef DqCfg<T, D, G> C;
+  return (size_t)C::NBUF * C::STAGE + (size_t)C::P * topk * 2;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
+    Shape s, const T* __restrict__ q, const unsigned char* __restrict__ bimg,
+    const int32_t* __restrict__ indices, const float* __restrict__ lse,
+    const float* __restrict__ delta, const T* __restrict__ dos, T* __restrict__ dq) {
+  typedef DqCfg<T, D, G> C;
+  constexpr int NT = C::NT, P = C::P, NSG = C::NSG, KS = C::KS, MT = C::MT;
+  constexpr int NFRAG = C::NFRAG, FCH = C::FCH, FRAG_BYTES = C::FRAG_BYTES, STAGE = C::STAGE;
+  constexpr int GB = C::GB, LOADS = C::LOADS;
+  typedef typename Frag<T>::type FragT;
+  typedef typename C::Img::K KI;  // fragment index helpers of the image
+  const float INF = __builtin_inff();
+
+  const int nblk_all = s.T / kBlock;
+  const int NTL = (s.T + P - 1) / P;
+  int bg, tile;
+  xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
+  const int t0 = tile * P;
+  const int nvalid = min(P, s.T - t0);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = threadIdx.x % kWave;
+  const int a = l / 16, col = l % 16;
+  const int sg = col / G, hh = col % G;
+  const int h = g * G + hh;
+  const float c1 = s.scale * kLog2e;
+  const int topk = s.topk;
+  const size_t q_row = (size_t)s.Hq * D;
+  const unsigned char* img_b = bimg + ((size_t)b * s.Hkv + g) * nblk_all * (size_t)STAGE;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ring = smem;                                                  // [NBUF][STAGE]
+  int16_t* lists = reinterpret_cast<int16_t*>(smem + (size_t)C::NBUF * STAGE);  // [P][topk]
+
+  for (int i = threadIdx.x; i < P * topk; i += NT) {
+    const int p = i / topk, e = i % topk;
+    const int j = p < nvalid ? indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e] : -1;
+    lists[i] = (int16_t)(j < 0 ? 0x7fff : j);
+  }
+
+  // this lane's row: position p, head h
+  const int pf = w * NSG;  // first position of the column group
+  const int p = pf + sg;
+  const int t = t0 + p;
+  const bool valid = p < nvalid;
+  const int own = (t0 + pf) / kBlock;
+  FragT qf[KS], df[KS];
+  float lse2 = INF, dl = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (valid) {
+      const size_t o = ((size_t)b * s.T + t) * q_row + (size_t)h * D + ks * 32 + 8 * a;
+      qf[ks] = Frag<T>::load(q + o);
+      df[ks] = Frag<T>::load(dos + o);
+    } else {
+      qf[ks] = Frag<T>::zero();
+      df[ks] = Frag<T>::zero();
+    }
+  }
+  if (valid) {
+    lse2 = lse[((size_t)b * s.Hq + h) * s.T + t] * kLog2e;
+    dl = delta[((size_t)b * s.Hq + h) * s.T + t];
+  }
+  __syncthreads();  // lists visible
+  int ptr = 0;
+  int nxt = valid ? lists[p * topk] : 0x7fff;
+  int nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+
+  const int c_last = (t0 + nvalid - 1) / kBlock;
+  const int nblk = c_last + 1;
+
+  auto issue = [&](int j, int bf) {
+    unsigned char* stage = ring + (size_t)bf * STAGE;
+    const unsigned char* src = img_b + (size_t)j * STAGE + 16 * l;
+    for (int pc = w; pc < LOADS; pc += C::NW)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024),
+                                       (void*)(stage + (size_t)pc * 1024), 16, 0, 0);
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4();
+
+  const int ngrp = (nblk + GB - 1) / GB;
+  auto issue_group = [&](int gi) {
+#pragma unroll
+    for (int qq = 0; qq < GB; ++qq)
+      if (gi * GB + qq < nblk) issue(gi * GB + qq, (gi & 1) * GB + qq);
+  };
+  issue_group(0);
+
+  for (int gi = 0; gi < ngrp; ++gi) {
+    wait_vmcnt<0>();       // this wave's loads of group gi (the only ones in flight)
+    barrier_keep_loads();  // all of group gi is in LDS; group gi-1's slots are free
+    if (gi + 1 < ngrp) issue_group(gi + 1);
+    for (int qq = 0; qq < GB; ++qq) {
+      const int j = gi * GB + qq;
+      if (j >= nblk) break;
+      if (j != nsel) continue;  // no row of this column group selected block j
+      const bool sl = nxt == j;
+      if (sl) {
+        ++ptr;
+        nxt = ptr < topk ? lists[p * topk + ptr] : 0x7fff;
+      }
+      nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+      const unsigned char* stage = ring + (size_t)((gi & 1) * GB + qq) * STAGE;
+
+      // S^T = K Q^T and dP^T = V dOs^T (K and V fragments in batches of FCH)
+      f32x4 st[4], dp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { st[u] = zero4(); dp[u] = zero4(); }
+#pragma unroll
+      for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
+        FragT kf[FCH], vf[FCH];
+#pragma unroll
+        for (int i = 0; i < FCH; ++i) {
+          kf[i] = lds_frag<T>(stage + (size_t)(f0 + i) * FRAG_BYTES, l);
+          vf[i] = lds_frag<T>(stage + (size_t)(NFRAG + f0 + i) * FRAG_BYTES, l);
+        }
+#pragma unroll
+        for (int i = 0; i < FCH; ++i) {
+          const int u = KI::k_u(f0 + i), ks = KI::k_ks(f0 + i);
+          st[u] = mma(st[u], kf[i], qf[ks]);
+          dp[u] = mma(dp[u], vf[i], df[ks]);
+        }
+      }
+
+      // dS = P (dP - Delta), P from the saved log-sum-exp; causal on the diagonal
+      const float lr = sl ? lse2 : INF;
+      FragT dsf[2];
+      if (j != own) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 2 * hf + e / 4, rr = e % 4;
+            const float pr = fast_exp2(st[u][rr] * c1 - lr);
+            x[e] = pr * (dp[u][rr] - dl);
+          }
+          dsf[hf] = Frag<T>::from_f32(x);
+        }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 2 * hf + e / 4, rr = e % 4;
+            const int key = j * kBlock + key_of(u, a, rr);
+            const float pr = key <= t ? fast_exp2(st[u][rr] * c1 - lr) : 0.f;
+            x[e] = pr * (dp[u][rr] - dl);
+          }
+          dsf[hf] = Frag<T>::from_f32(x);
+        }
+      }
+
+      // dq^T += K^T dS^T (K^T fragments in batches)
+#pragma unroll
+      for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
+        FragT tf[FCH];
+#pragma unroll
+        for (int i = 0; i < FCH; ++i) tf[i] = lds_frag<T>(stage + (size_t)(2 * NFRAG + f0 + i) * FRAG_BYTES, l);
+#pragma unroll
+        for (int i = 0; i < FCH; ++i)
+          acc[KI::v_mt(f0 + i)] = mma(acc[KI::v_mt(f0 + i)], tf[i], dsf[KI::v_h(f0 + i)]);
+      }
+    }
+  }
+
+  if (valid) {
+    T* dst = dq + ((size_t)b * s.T + t) * q_row + (size_t)h * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) store4(dst + mt * 16 + 4 * a, acc[mt] * s.scale);
+  }
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_dq_t(const Shape& s, const void* q, const void* bimg, const int32_t* idx,
+                              const float* lse, const float* delta, const void* dos, void* dq,
+                              hipStream_t st) {
+  typedef DqCfg<T, D, G> C;
+  const size_t lds = dq_lds_bytes<T, D, G>(s.topk);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, G>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((s.T + C::P - 1) / C::P * s.Hkv * s.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, G>), grid, dim3(C::NT), lds, st, s, (const T*)q,
+                     (const unsigned char*)bimg, idx, lse, delta, (const T*)dos, (T*)dq);
+  return hipGetLastError();
+}
+template <typename T, int D>
+static hipError_t launch_dq_g(const Shape& s, const void* q, const void* bimg, const int32_t* idx,
+                              const float* lse, const float* delta, const void* dos, void* dq,
+                              hipStream_t st) {
+  switch (s.G) {
+    case 1: return launch_dq_t<T, D, 1>(s, q, bimg, idx, lse, delta, dos, dq, st);
+    case 2: return launch_dq_t<T, D, 2>(s, q, bimg, idx, lse, delta, dos, dq, st);
+    case 4: return launch_dq_t<T, D, 4>(s, q, bimg, idx, lse, delta, dos, dq, st);
+    case 8: return launch_dq_t<T, D, 8>(s, q, bimg, idx, lse, delta, dos, dq, st);
+    default: return launch_dq_t<T, D, 16>(s, q, bimg, idx, lse, delta, dos, dq, st);
+  }
+}
+
+hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
+                         const int32_t* indices, const float* lse, const float* delta,
+                         const void* dos, void* dq, hipStream_t st) {
+  if (is_bf16) {
+    if (s.D == 64) return launch_dq_g<bf16, 64>(s, q, bimg, indices, lse, delta, dos, dq, st);
+    return launch_dq_g<bf16, 128>(s, q, bimg, indices, lse, delta, dos, dq, st);
+  }
+  return launch_dq_g<float, 64>(s, q, bimg, indices, lse, delta, dos, dq, st);
+}
+
+}  // namespace nsa

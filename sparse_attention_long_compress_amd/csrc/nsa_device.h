@@ -177,6 +177,95 @@ struct KvImage {
   }
 };
 
+// Staged image of one 64-key block for the query-stationary backward (dq):
+// K, V and K^T as MFMA fragments, one after the other.  Fragment f < NFRAG
+// is K subtile u = f % 4 at k step ks = f / 4 (as in KvImage); fragment
+// NFRAG + f is the same for V; fragment 2 NFRAG + h (D / 16) + mt is K^T
+// channel tile mt over keys 32 h .. 32 h + 31 (the A operand of dq^T =
+// K^T dS^T).  Pieces of 64 lanes x 16 bytes, as in KvImage.
+template <typename T, int D>
+struct BwdImage {
+  typedef KvImage<T, D> K;
+  static constexpr int NV = K::NV, EPV = K::EPV, KS = K::KS, NFRAG = K::NFRAG, MT = K::MT;
+  static constexpr int PIECES = 3 * NFRAG * NV;
+  static constexpr int BYTES = PIECES * 1024;
+};
+
+// ---- helpers of the block-walking kernels (selection/window forward, dq) ----
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier that is also a compiler memory barrier but, unlike
+// __syncthreads, does not drain the outstanding global->LDS loads.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// lane fragment (8 elements) stored as [NV][64 lanes][16 bytes] in LDS
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type lds_frag(const unsigned char* base, int l);
+template <>
+__device__ __forceinline__ bf16x8 lds_frag<bf16>(const unsigned char* base, int l) {
+  return *reinterpret_cast<const bf16x8*>(base + 16 * l);
+}
+template <>
+__device__ __forceinline__ f32x8 lds_frag<float>(const unsigned char* base, int l) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(base + 16 * l);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(base + 1024 + 16 * l);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+  return r;
+}
+
+// Sum of the 8 probabilities of a B fragment (the values the PV MFMA uses).
+__device__ __forceinline__ float frag_sum(const bf16x8& p) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {p[2 * i], p[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& p) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += p[i];
+  return s;
+}
+// lanes whose condition is false get an all-zero fragment
+__device__ __forceinline__ bf16x8 frag_keep(const bf16x8& p, bool keep) {
+  typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+  u32x4 u = __builtin_bit_cast(u32x4, p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = keep ? u[i] : 0u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f32x8 frag_keep(const f32x8& p, bool keep) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = keep ? p[i] : 0.f;
+  return r;
+}
+
+// minimum over each 16-lane row (DPP butterfly; every lane gets its row's minimum)
+__device__ __forceinline__ int row_min16(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true));  // other quad of 8
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true));  // other half of 16
+  return v;
+}
+
+// key (0..63 within the block) of C-layout element (subtile u, register r) in lane group a
+__device__ __forceinline__ int key_of(int u, int a, int r) { return 32 * (u >> 1) + 8 * a + 4 * (u & 1) + r; }
+
 // Work order for a 1-D grid over (batch * kv-group) x tiles.  Workgroups are
 // dealt to the 8 XCDs round-robin (XCD = id % 8), each XCD with its own L2.
 // When the number of (batch, group) pairs NBG divides 8 or is a multiple of

@@ -38,15 +38,16 @@ hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const voi
                           void* o_sel, hipStream_t st);
 
 // Backward (selection branch).
-hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* gates,
-                           const void* o_sel, const void* dout, void* kt, float* delta,
-                           void* dos, hipStream_t st);
+//   prep: bimg [B][Hkv][T/64][BwdImage<T, D>::BYTES] (K, V, K^T fragments of
+//   each key block), delta [B][Hq][T] fp32, dos [B][T][Hq][D].
+hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* v,
+                           const void* gates, const void* o_sel, const void* dout, void* bimg,
+                           float* delta, void* dos, hipStream_t st);
 hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* revmap,
                              hipStream_t st);
-hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* k,
-                         const void* kt, const void* v, const int32_t* indices,
-                         const float* lse, const float* delta, const void* dos, void* dq,
-                         hipStream_t st);
+hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
+                         const int32_t* indices, const float* lse, const float* delta,
+                         const void* dos, void* dq, hipStream_t st);
 hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* k,
                            const void* v, const float* lse, const float* delta, const void* dos,
                            const uint64_t* revmap, void* dk, void* dv, void* items_ws,
