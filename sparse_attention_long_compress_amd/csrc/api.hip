@@ -245,7 +245,7 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   e = nsa::launch_bwd_dq(bf, s, q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta),
                          ws + L.dos, dq, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_dkdv(bf, s, q, k, v, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
+  e = nsa::launch_bwd_dkdv(bf, s, q, ws + L.bimg, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
                            (const uint64_t*)(ws + L.revmap), dk, dv, ws + L.items,
                            (int*)(ws + L.slots), (float*)(ws + L.part), hs);
   return launched(e);

@@ -48,8 +48,8 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
 hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
                          const int32_t* indices, const float* lse, const float* delta,
                          const void* dos, void* dq, hipStream_t st);
-hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* k,
-                           const void* v, const float* lse, const float* delta, const void* dos,
+hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* bimg,
+                           const float* lse, const float* delta, const void* dos,
                            const uint64_t* revmap, void* dk, void* dv, void* items_ws,
                            int* slot_base, float* part, hipStream_t st);
 size_t bwd_items_bytes(int nblk);
