@@ -1,7 +1,7 @@
 // api.hip -- the C ABI declared in include/nsa.h: parameter checks, workspace
 // carving and launch sequencing.  Nothing here computes; every step of the
 // path runs in the gfx950 kernels (pool.hip, cmp_select.hip, sel_win.hip,
-// bwd.hip).  No allocation, no synchronisation, no global mutable state.
+// bwd.hip, bwd_dq.hip, bwd_dkdv.hip).  No allocation, no synchronisation, no global mutable state.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -73,19 +73,23 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
 
 // Backward workspace regions.
 struct BwdLayout {
-  size_t bimg, delta, dos, revmap, items, slots, part, total;
+  size_t bimg, delta, dos, revmap, lists, counts, items, slot_base, slot_cnt, nitems, part, total;
 };
 BwdLayout bwd_layout(const Shape& s, size_t es) {
   BwdLayout L;
   size_t o = 0;
-  const size_t nblk = s.T / 64;
-  L.bimg = o;   o += up((size_t)s.B * s.Hkv * nblk * 3 * 64 * s.D * es, kAlign);
-  L.delta = o;  o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
-  L.dos = o;    o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
-  L.revmap = o; o += up((size_t)s.B * s.Hkv * nblk * nblk * 8, kAlign);
-  L.items = o;  o += up(nsa::bwd_items_bytes((int)nblk), kAlign);
-  L.slots = o;  o += up(nblk * 4, kAlign);
-  L.part = o;   o += up(nsa::bwd_part_floats(s) * 4, kAlign);
+  const size_t nblk = s.T / 64, NJ = (size_t)s.B * s.Hkv * nblk;
+  L.bimg = o;      o += up(NJ * 3 * 64 * s.D * es, kAlign);
+  L.delta = o;     o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
+  L.dos = o;       o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
+  L.revmap = o;    o += up(NJ * nblk * 8, kAlign);
+  L.lists = o;     o += up(NJ * s.T * 2, kAlign);
+  L.counts = o;    o += up(NJ * 4, kAlign);
+  L.items = o;     o += up(nsa::bwd_items_bytes(s), kAlign);
+  L.slot_base = o; o += up(NJ * 4, kAlign);
+  L.slot_cnt = o;  o += up(NJ * 4, kAlign);
+  L.nitems = o;    o += up(4, kAlign);
+  L.part = o;      o += up(nsa::bwd_part_floats(s) * 4, kAlign);
   L.total = o;
   return L;
 }
@@ -245,9 +249,16 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   e = nsa::launch_bwd_dq(bf, s, q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta),
                          ws + L.dos, dq, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  nsa::BwdPlanWs pw;
+  pw.items = ws + L.items;
+  pw.lists = (uint16_t*)(ws + L.lists);
+  pw.counts = (int*)(ws + L.counts);
+  pw.slot_base = (int*)(ws + L.slot_base);
+  pw.slot_cnt = (int*)(ws + L.slot_cnt);
+  pw.nitems = (int*)(ws + L.nitems);
+  pw.part = (float*)(ws + L.part);
   e = nsa::launch_bwd_dkdv(bf, s, q, ws + L.bimg, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
-                           (const uint64_t*)(ws + L.revmap), dk, dv, ws + L.items,
-                           (int*)(ws + L.slots), (float*)(ws + L.part), hs);
+                           (const uint64_t*)(ws + L.revmap), dk, dv, pw, hs);
   return launched(e);
 }
 

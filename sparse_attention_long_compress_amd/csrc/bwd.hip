@@ -80,45 +80,53 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
     }
     *reinterpret_cast<f32x4*>(img + (size_t)pc * 1024 + 16 * l) = *reinterpret_cast<const f32x4*>(piece);
   }
-  // dOs and Delta for the G heads of the group: one wave per (position, head) row
-  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  for (int row = w; row < kBlock * G; row += 4) {
+  // dOs and Delta for the G heads of the group: D / EPV consecutive lanes per
+  // (position, head) row, 16-byte accesses
+  constexpr int TPR = D / EPV;
+  static_assert((kBlock * TPR) % 256 == 0, "whole passes");
+#pragma unroll 4
+  for (int i = threadIdx.x; i < kBlock * G * TPR; i += 256) {
+    const int row = i / TPR, c = i % TPR;
     const int t = j * kBlock + row / G, h = g * G + row % G;
-    const size_t base = (((size_t)b * s.T + t) * s.Hq + h) * D;
+    const size_t base = (((size_t)b * s.T + t) * s.Hq + h) * D + c * EPV;
     const float gs = (float)gates[(((size_t)b * s.T + t) * s.Hq + h) * 3 + 1];
+    const Vec dv = *reinterpret_cast<const Vec*>(dout + base);
+    const Vec ov = *reinterpret_cast<const Vec*>(o_sel + base);
+    Vec outv;
     float acc = 0.f;
-    for (int d = l; d < D; d += kWave) {
-      const float v_ = gs * (float)dout[base + d];
-      dos[base + d] = (T)v_;
-      acc += v_ * (float)o_sel[base + d];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float x = gs * (float)dv[e];
+      outv[e] = (T)x;
+      acc += x * (float)ov[e];
     }
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (l == 0) delta[((size_t)b * s.Hq + h) * s.T + t] = acc;
+    *reinterpret_cast<Vec*>(dos + base) = outv;
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0) delta[((size_t)b * s.Hq + h) * s.T + t] = acc;
   }
 }
 
 // ============================================================ B1: reverse map
-// grid (nblk tiles c, Hkv, B), 64 threads.  revmap[b][g][j][c] for j <= c.
+// grid (nblk tiles c, Hkv, B), 64 threads (lane = position of the tile).
+// revmap[b][g][j][c] for j <= c, built with 64-bit LDS ORs.
 __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* __restrict__ idx,
                                                         uint64_t* __restrict__ revmap) {
-  extern __shared__ unsigned char bits[];  // [c+1][64]
+  extern __shared__ unsigned long long msk[];  // [c + 1]
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nblk = s.T / kBlock;
   const int l = threadIdx.x;
-  for (int i = l; i < (c + 1) * 64; i += 64) bits[i] = 0;
+  for (int i = l; i <= c; i += 64) msk[i] = 0ull;
   __syncthreads();
   const int t = c * kBlock + l;
   const int32_t* row = idx + (((size_t)b * s.Hkv + g) * s.T + t) * s.topk;
   for (int e = 0; e < s.topk; ++e) {
     const int j = row[e];
-    if (j >= 0 && j <= c) bits[j * 64 + l] = 1;
+    if (j >= 0 && j <= c) atomicOr(&msk[j], 1ull << l);
   }
   __syncthreads();
-  uint64_t* dst = revmap + (((size_t)b * s.Hkv + g) * nblk) * nblk;
-  for (int j = 0; j <= c; ++j) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(bits[j * 64 + l] != 0);
-    if (l == 0) dst[(size_t)j * nblk + c] = m;
-  }
+  uint64_t* dst = revmap + (((size_t)b * s.Hkv + g) * nblk) * nblk + c;
+  for (int j = l; j <= c; j += 64) dst[(size_t)j * nblk] = msk[j];
 }
 
 // ============================================================ launchers
@@ -148,7 +156,7 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
                              hipStream_t st) {
   const int nblk = s.T / kBlock;
   dim3 grid(nblk, s.Hkv, s.B);
-  hipLaunchKernelGGL(bwd_revmap_kernel, grid, dim3(64), (size_t)nblk * 64, st, s, indices, revmap);
+  hipLaunchKernelGGL(bwd_revmap_kernel, grid, dim3(64), (size_t)nblk * 8, st, s, indices, revmap);
   return hipGetLastError();
 }
 

@@ -34,103 +34,121 @@
 namespace nsa {
 
 // ------------------------------------------------------------------ items
+// The rows of block j are the positions that selected it (ascending, from the
+// reverse map) times the G heads of the group.  A block's position list is
+// cut into items of about kItemRows rows (at most kMaxItemPos positions, the
+// LDS list of the dk/dv kernel); blocks with several items get one partial
+// slot per item.
 struct Item {
-  int j, c_lo, c_hi, slot;
+  int bg, j, lo, hi, slot;  // (batch, group) index, block, positions [lo, hi) of its list, slot or -1
 };
 
-constexpr int kMaxSegTiles = 32;  // query tiles per item at most (bounds the LDS position list)
+constexpr int kItemRows = 2048;
+constexpr int kMaxItemPos = 2048;
 
-// Query tiles that can read block j are c >= j.  Block 0, read by every
-// position, is cut into runs of 8 tiles; block j >= 1 into the geometric runs
-// [j, 2j), [2j, 4j), ... (each holds about the same expected number of
-// selecting rows when the selection probability falls like 1 / position),
-// each run cut further into pieces of at most kMaxSegTiles tiles.  The same
-// functions run on the host (sizing) and on the device (item table).
-__host__ __device__ inline int segments_of(int j, int nblk) {
-  if (j == 0) return (nblk + 7) / 8;
-  int n = 0;
-  for (long lo = j; lo < nblk; lo *= 2) {
-    const long hi = lo * 2 < nblk ? lo * 2 : nblk;
-    n += (int)((hi - lo + kMaxSegTiles - 1) / kMaxSegTiles);
-  }
-  return n;
+__host__ __device__ inline int items_of(int npos, int G) {
+  int n = (npos * G + kItemRows - 1) / kItemRows;
+  const int m = (npos + kMaxItemPos - 1) / kMaxItemPos;
+  n = n > m ? n : m;
+  return n > 1 ? n : 1;
 }
-__host__ __device__ inline void segment_range(int j, int i, int nblk, int& lo_out, int& hi_out) {
-  if (j == 0) {
-    lo_out = 8 * i;
-    hi_out = 8 * i + 8 < nblk ? 8 * i + 8 : nblk;
-    return;
-  }
-  for (long lo = j; lo < nblk; lo *= 2) {
-    const long hi = lo * 2 < nblk ? lo * 2 : nblk;
-    const int np = (int)((hi - lo + kMaxSegTiles - 1) / kMaxSegTiles);
-    if (i < np) {
-      const long len = hi - lo;
-      lo_out = (int)(lo + len * i / np);
-      hi_out = (int)(lo + len * (i + 1) / np);
-      return;
+
+// Upper bound on the item count (grid size; workspace): a block has at most
+// 1 + rows / kItemRows items, and every position selects at most top_k blocks.
+int bwd_item_bound(const Shape& s) {
+  const long nblk = s.T / kBlock;
+  const long rows = (long)s.T * s.topk * s.G;
+  return (int)((long)s.B * s.Hkv * (nblk + (rows + kItemRows - 1) / kItemRows));
+}
+
+// B1b: grid (nblk, Hkv, B), 256 threads.  Ascending positions that selected
+// block j -> lists[b][g][j][0 .. P_j) (capacity T), counts[b][g][j] = P_j.
+__global__ __launch_bounds__(256) void bwd_lists_kernel(Shape s, const uint64_t* __restrict__ revmap,
+                                                        uint16_t* __restrict__ lists,
+                                                        int* __restrict__ counts) {
+  __shared__ uint64_t msk[256];
+  __shared__ int off[256];
+  __shared__ int wsum[4];
+  __shared__ int carry;
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nblk = s.T / kBlock;
+  const size_t e = ((size_t)b * s.Hkv + g) * nblk + j;
+  const uint64_t* rm = revmap + e * nblk;
+  uint16_t* out = lists + e * (size_t)s.T;
+  const int x = threadIdx.x, w = x / 64, l = x % 64;
+  if (x == 0) carry = 0;
+  __syncthreads();
+  for (int c0 = j; c0 < nblk; c0 += 256) {
+    const uint64_t m = c0 + x < nblk ? rm[c0 + x] : 0ull;
+    const int n = __popcll(m);
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (l >= o) incl += y;
     }
-    i -= np;
+    if (l == 63) wsum[w] = incl;
+    msk[x] = m;
+    __syncthreads();
+    int pre = carry;
+    for (int k = 0; k < w; ++k) pre += wsum[k];
+    off[x] = pre + incl - n;
+    __syncthreads();
+    if (x == 255) carry = pre + incl;
+    const int nt = min(256, nblk - c0);
+    for (int ti = w; ti < nt; ti += 4) {
+      const uint64_t mm = msk[ti];
+      if ((mm >> l) & 1ull) out[off[ti] + __popcll(mm & ((1ull << l) - 1ull))] = (uint16_t)((c0 + ti) * kBlock + l);
+    }
+    __syncthreads();
   }
-  lo_out = hi_out = nblk;
+  if (x == 0) counts[e] = carry;
 }
 
-int bwd_item_count(int nblk) {
-  int n = 0;
-  for (int j = 0; j < nblk; ++j) n += segments_of(j, nblk);
-  return n;
-}
-int bwd_slot_count(int nblk) {
-  int n = 0;
-  for (int j = 0; j < nblk; ++j) {
-    const int ns = segments_of(j, nblk);
-    if (ns > 1) n += ns;
-  }
-  return n;
-}
-
-// Item table and the first partial slot of every block (-1: one item, no
-// partials).  One workgroup; exclusive scans over the blocks, 1024 at a time.
-__global__ __launch_bounds__(1024) void bwd_items_kernel(int nblk, Item* __restrict__ items,
-                                                        int* __restrict__ slot_base) {
-  __shared__ int sc[1024], ss[1024];
+// B1c: one workgroup.  Items of every (batch, group, block) in natural order
+// (block-major), slot_base / slot_cnt per block and the item count.
+__global__ __launch_bounds__(1024) void bwd_items_kernel(int NJ, int nblk, int G, const int* __restrict__ counts,
+                                                        Item* __restrict__ items, int* __restrict__ slot_base,
+                                                        int* __restrict__ slot_cnt, int* __restrict__ nitems) {
+  __shared__ int wtot[2][16];
   __shared__ int carry[2];
-  const int x = threadIdx.x;
+  const int x = threadIdx.x, w = x / 64, l = x % 64;
   if (x == 0) carry[0] = carry[1] = 0;
   __syncthreads();
-  for (int j0 = 0; j0 < nblk; j0 += 1024) {
-    const int j = j0 + x;
-    const int ns = j < nblk ? segments_of(j, nblk) : 0;
-    const int sl = ns > 1 ? ns : 0;
-    sc[x] = ns;
-    ss[x] = sl;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int a = x >= off ? sc[x - off] : 0;
-      const int c = x >= off ? ss[x - off] : 0;
-      __syncthreads();
-      sc[x] += a;
-      ss[x] += c;
-      __syncthreads();
+  for (int e0 = 0; e0 < NJ; e0 += 1024) {
+    const int e = e0 + x;
+    const int P = e < NJ ? counts[e] : 0;
+    const int n = e < NJ ? items_of(P, G) : 0;
+    const int sl = n > 1 ? n : 0;
+    int in = n, is = sl;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(in, o), z = __shfl_up(is, o);
+      if (l >= o) { in += y; is += z; }
     }
-    const int io = carry[0] + sc[x] - ns, so = carry[1] + ss[x] - sl;
-    if (j < nblk) {
-      slot_base[j] = ns > 1 ? so : -1;
-      for (int i = 0; i < ns; ++i) {
+    if (l == 63) { wtot[0][w] = in; wtot[1][w] = is; }
+    __syncthreads();
+    int pi = carry[0], ps = carry[1];
+    for (int k = 0; k < w; ++k) { pi += wtot[0][k]; ps += wtot[1][k]; }
+    const int io = pi + in - n, so = ps + is - sl;
+    if (e < NJ) {
+      slot_base[e] = n > 1 ? so : -1;
+      slot_cnt[e] = n;
+      for (int i = 0; i < n; ++i) {
         Item it;
-        it.j = j;
-        segment_range(j, i, nblk, it.c_lo, it.c_hi);
-        it.slot = ns > 1 ? so + i : -1;
+        it.bg = e / nblk;
+        it.j = e % nblk;
+        it.lo = P * i / n;  // P <= 65536, n <= P: no overflow
+        it.hi = P * (i + 1) / n;
+        it.slot = n > 1 ? so + i : -1;
         items[io + i] = it;
       }
     }
     __syncthreads();
-    if (x == 1023) {
-      carry[0] += sc[1023];
-      carry[1] += ss[1023];
-    }
+    if (x == 1023) { carry[0] = pi + in; carry[1] = ps + is; }
     __syncthreads();
   }
+  if (x == 0) *nitems = carry[0];
 }
 
 // ------------------------------------------------------------------ B3
@@ -156,9 +174,9 @@ struct KvCfg {
   static constexpr int KVB = 2 * NFRAG * FRAG_BYTES;  // K and V fragments of the block image
   static constexpr int KS = D / 32, MT = D / 16;
   static constexpr int NFR = 4 * MT;                  // accumulator fragments per tensor
-  static constexpr int MAXPOS = kMaxSegTiles * kBlock;
+  static constexpr int MAXPOS = kMaxItemPos;
   static constexpr size_t RING = (size_t)NW * NR * STAGE;
-  static constexpr size_t LDS = KVB + RING + MAXPOS * 2 + 64 * 4;
+  static constexpr size_t LDS = KVB + RING + MAXPOS * 2;
   static_assert(CP >= 1 && CP * G == CR, "a chunk holds whole positions");
   static_assert(RING >= (size_t)NW * NFR * 1024, "reduction fits in the ring");
   static_assert((NR - 1) * LQ < 64, "vmcnt range");
@@ -245,8 +263,8 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
     Shape s, const Item* __restrict__ items, const T* __restrict__ q,
     const unsigned char* __restrict__ bimg, const float* __restrict__ lse,
-    const float* __restrict__ delta, const T* __restrict__ dos, const uint64_t* __restrict__ revmap,
-    T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ part, int nslots) {
+    const float* __restrict__ delta, const T* __restrict__ dos, const uint16_t* __restrict__ lists,
+    const int* __restrict__ nitems, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ part) {
   typedef KvCfg<T, D, G> C;
   constexpr int NW = C::NW, NT = C::NT, CP = C::CP, TB = C::TB, NLD = C::NLD, RPI = C::RPI;
   constexpr int SLOTS = C::SLOTS, LQ = C::LQ, STAGE = C::STAGE, NR = C::NR;
@@ -260,11 +278,12 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
   unsigned char* kv = smem;                                    // [KVB]
   unsigned char* ring = smem + KVB;                            // [NW][NR][STAGE]
   uint16_t* plist = reinterpret_cast<uint16_t*>(ring + C::RING);  // [MAXPOS]
-  int* toff = reinterpret_cast<int*>(plist + C::MAXPOS);          // [64]
 
-  const int nblk = s.T / kBlock;
+  // items in block-major order (an XCD-interleaved order measured slower)
+  if ((int)blockIdx.x >= *nitems) return;
   const Item it = items[blockIdx.x];
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int nblk = s.T / kBlock;
+  const int g = it.bg % s.Hkv, b = it.bg / s.Hkv;
   const int j = it.j;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = threadIdx.x % kWave;
@@ -274,31 +293,16 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
 
   // K and V fragments of block j (first 2 NFRAG fragments of its backward image)
   {
-    const unsigned char* src = bimg + (((size_t)b * s.Hkv + g) * nblk + j) * (size_t)BwdImage<T, D>::BYTES + 16 * l;
+    const unsigned char* src = bimg + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES + 16 * l;
     for (int pc = w; pc < KVB / 1024; pc += NW)
       __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024), (void*)(kv + (size_t)pc * 1024),
                                        16, 0, 0);
   }
-  // ascending list of the positions of tiles [c_lo, c_hi) that selected block j
-  const uint64_t* rm = revmap + (((size_t)b * s.Hkv + g) * nblk + j) * nblk;
-  const int ntile = it.c_hi - it.c_lo;
-  if (w == 0) {
-    const uint64_t msk = l < ntile ? rm[it.c_lo + l] : 0ull;
-    int n = __popcll(msk), incl = n;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (l >= off) incl += y;
-    }
-    toff[l] = incl - n;
-    if (l == 63) toff[63] = incl;  // total (tiles never fill all 64 lanes: ntile <= 32)
-  }
-  __syncthreads();
-  const int npos = toff[63];
-  for (int ti = w; ti < ntile; ti += NW) {
-    const uint64_t msk = rm[it.c_lo + ti];
-    if ((msk >> l) & 1ull)
-      plist[toff[ti] + __popcll(msk & ((1ull << l) - 1ull))] = (uint16_t)((it.c_lo + ti) * kBlock + l);
+  // the item's slice of the block's ascending position list
+  const int npos = it.hi - it.lo;
+  {
+    const uint16_t* src = lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
+    for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -432,9 +436,12 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
     }
   }
 
-  // sum the waves' accumulators through LDS (the rings are free now) and write
+  // sum the waves' accumulators through LDS (the rings are free now) and write:
+  // the only item of a block writes dk / dv (rows staged in LDS for 16-byte
+  // stores), the others their fp32 partial in fragment order
   __syncthreads();
   float* red = reinterpret_cast<float*>(ring);
+  constexpr int OWN = (NFR + NW - 1) / NW;  // fragments summed per wave
   const size_t k_row = (size_t)s.Hkv * D;
 #pragma unroll
   for (int tns = 0; tns < 2; ++tns) {
@@ -442,21 +449,38 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
     for (int fi = 0; fi < NFR; ++fi)
       *reinterpret_cast<f32x4*>(red + ((size_t)(w * NFR + fi) * 64 + l) * 4) = tns == 0 ? adk[fi] : adv[fi];
     __syncthreads();
-    for (int fi = w; fi < NFR; fi += NW) {
-      f32x4 sum = *reinterpret_cast<const f32x4*>(red + ((size_t)fi * 64 + l) * 4);
-      for (int w2 = 1; w2 < NW; ++w2) sum += *reinterpret_cast<const f32x4*>(red + ((size_t)(w2 * NFR + fi) * 64 + l) * 4);
-      if (it.slot < 0) {
-        const int v = fi / MT, m = fi % MT;
-        T* dst = tns == 0 ? dk : dv;
-        const float sc = tns == 0 ? s.scale : 1.f;
+    f32x4 sum[OWN];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = j * kBlock + KI::krow(v, 4 * a + r);
-          dst[((size_t)b * s.T + kk) * k_row + (size_t)g * D + 16 * m + col] = (T)(sum[r] * sc);
+    for (int o = 0; o < OWN; ++o) {
+      const int fi = w + o * NW;
+      sum[o] = zero4();
+      if (fi < NFR)
+        for (int w2 = 0; w2 < NW; ++w2) sum[o] += *reinterpret_cast<const f32x4*>(red + ((size_t)(w2 * NFR + fi) * 64 + l) * 4);
+    }
+    __syncthreads();
+    if (it.slot >= 0) {
+      float* ps = part + ((size_t)it.slot * 2 + tns) * (size_t)NFR * 256;
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int fi = w + o * NW;
+        if (fi < NFR) *reinterpret_cast<f32x4*>(ps + ((size_t)fi * 64 + l) * 4) = sum[o];
+      }
+    } else {
+      const float sc = tns == 0 ? s.scale : 1.f;
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int fi = w + o * NW;
+        if (fi < NFR) {
+          const int v = fi / MT, m = fi % MT;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[KI::krow(v, 4 * a + r) * D + 16 * m + col] = sum[o][r] * sc;
         }
-      } else {
-        float* ps = part + ((((size_t)b * s.Hkv + g) * (size_t)nslots + it.slot) * 2 + tns) * (size_t)NFR * 256;
-        *reinterpret_cast<f32x4*>(ps + ((size_t)fi * 64 + l) * 4) = sum;
+      }
+      __syncthreads();
+      T* dst = (tns == 0 ? dk : dv) + ((size_t)b * s.T + j * kBlock) * k_row + (size_t)g * D;
+      for (int i = threadIdx.x; i < kBlock * D / 8; i += NT) {
+        const int kk = i / (D / 8), c8 = (i % (D / 8)) * 8;
+        store8(dst + (size_t)kk * k_row + c8, red + kk * D + c8);
       }
     }
     __syncthreads();
@@ -464,101 +488,121 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ B4
-// grid (nblk, Hkv, B): the partial sums of a block's items, in item order.
+// grid (B Hkv nblk): the partial sums of a block's items, added in item order,
+// rows staged in LDS for 16-byte stores.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Shape s, const int* __restrict__ slot_base,
-                                                         const float* __restrict__ part, int nslots,
+                                                         const int* __restrict__ slot_cnt,
+                                                         const float* __restrict__ part,
                                                          T* __restrict__ dk, T* __restrict__ dv) {
   typedef typename BwdImage<T, D>::K KI;
   constexpr int MT = D / 16, NFR = 4 * MT;
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int nblk = s.T / kBlock;
-  const int base = slot_base[j];
+  constexpr int PER = 2 * NFR * 64 / 256;  // fragment entries (4 floats) per thread
+  __shared__ __align__(16) float ot[2][kBlock * D];
+  const int e = blockIdx.x;
+  const int base = slot_base[e];
   if (base < 0) return;
-  const int ns = segments_of(j, nblk);
-  const size_t k_row = (size_t)s.Hkv * D;
-  const float* pb = part + (((size_t)b * s.Hkv + g) * (size_t)nslots + base) * 2 * (size_t)NFR * 256;
-  for (int i = threadIdx.x; i < 2 * NFR * 64; i += 256) {
+  const int ns = slot_cnt[e];
+  const int nblk = s.T / kBlock;
+  const int bg = e / nblk, j = e % nblk;
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
+  const float* pb = part + (size_t)base * 2 * NFR * 256;
+  f32x4 sum[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sum[k] = *reinterpret_cast<const f32x4*>(pb + ((size_t)threadIdx.x + 256 * k) * 4);
+  for (int z = 1; z < ns; ++z) {
+    const float* pz = pb + (size_t)z * 2 * NFR * 256;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) sum[k] += *reinterpret_cast<const f32x4*>(pz + ((size_t)threadIdx.x + 256 * k) * 4);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k;
     const int tns = i / (NFR * 64), fi = (i / 64) % NFR, l = i % 64;
-    f32x4 sum = *reinterpret_cast<const f32x4*>(pb + (size_t)i * 4);
-    for (int z = 1; z < ns; ++z) sum += *reinterpret_cast<const f32x4*>(pb + ((size_t)z * 2 * NFR * 64 + i) * 4);
     const int v = fi / MT, m = fi % MT, a = l >> 4, col = l & 15;
-    T* dst = tns == 0 ? dk : dv;
     const float sc = tns == 0 ? s.scale : 1.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = j * kBlock + KI::krow(v, 4 * a + r);
-      dst[((size_t)b * s.T + kk) * k_row + (size_t)g * D + 16 * m + col] = (T)(sum[r] * sc);
-    }
+    for (int r = 0; r < 4; ++r) ot[tns][KI::krow(v, 4 * a + r) * D + 16 * m + col] = sum[k][r] * sc;
+  }
+  __syncthreads();
+  const size_t k_row = (size_t)s.Hkv * D;
+  for (int i = threadIdx.x; i < 2 * kBlock * D / 8; i += 256) {
+    const int tns = i / (kBlock * D / 8), i2 = i % (kBlock * D / 8);
+    const int kk = i2 / (D / 8), c8 = (i2 % (D / 8)) * 8;
+    T* dst = (tns == 0 ? dk : dv) + ((size_t)b * s.T + j * kBlock + kk) * k_row + (size_t)g * D + c8;
+    store8(dst, &ot[tns][kk * D + c8]);
   }
 }
 
 // ------------------------------------------------------------------ launchers
 template <typename T, int D, int G>
-static hipError_t launch_kv_t(const Shape& s, const Item* items, int nitems, int nslots, const void* q,
-                              const void* bimg, const float* lse, const float* delta, const void* dos,
-                              const uint64_t* revmap, void* dk, void* dv, float* part, hipStream_t st) {
+static hipError_t launch_kv_t(const Shape& s, const Item* items, int grid_items, const int* nitems,
+                              const void* q, const void* bimg, const float* lse, const float* delta,
+                              const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+                              hipStream_t st) {
   typedef KvCfg<T, D, G> C;
   hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, G>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return e;
-  dim3 grid(nitems, s.Hkv, s.B);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, G>), grid, dim3(C::NT), C::LDS, st, s, items, (const T*)q,
-                     (const unsigned char*)bimg, lse, delta, (const T*)dos, revmap, (T*)dk, (T*)dv,
-                     part, nslots);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, G>), dim3(grid_items), dim3(C::NT), C::LDS, st, s, items,
+                     (const T*)q, (const unsigned char*)bimg, lse, delta, (const T*)dos, lists, nitems,
+                     (T*)dk, (T*)dv, part);
   return hipGetLastError();
 }
 template <typename T, int D>
-static hipError_t launch_kv_g(const Shape& s, const Item* items, int nitems, int nslots, const void* q,
-                              const void* bimg, const float* lse, const float* delta, const void* dos,
-                              const uint64_t* revmap, void* dk, void* dv, float* part, hipStream_t st) {
+static hipError_t launch_kv_g(const Shape& s, const Item* items, int grid_items, const int* nitems,
+                              const void* q, const void* bimg, const float* lse, const float* delta,
+                              const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+                              hipStream_t st) {
+#define NSA_KV(GG) launch_kv_t<T, D, GG>(s, items, grid_items, nitems, q, bimg, lse, delta, dos, lists, dk, dv, part, st)
   switch (s.G) {
-    case 1: return launch_kv_t<T, D, 1>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
-    case 2: return launch_kv_t<T, D, 2>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
-    case 4: return launch_kv_t<T, D, 4>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
-    case 8: return launch_kv_t<T, D, 8>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
-    default: return launch_kv_t<T, D, 16>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
+    case 1: return NSA_KV(1);
+    case 2: return NSA_KV(2);
+    case 4: return NSA_KV(4);
+    case 8: return NSA_KV(8);
+    default: return NSA_KV(16);
   }
+#undef NSA_KV
 }
 
 hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* bimg,
                            const float* lse, const float* delta, const void* dos,
-                           const uint64_t* revmap, void* dk, void* dv, void* items_ws,
-                           int* slot_base, float* part, hipStream_t st) {
+                           const uint64_t* revmap, void* dk, void* dv, const BwdPlanWs& ws,
+                           hipStream_t st) {
   const int nblk = s.T / kBlock;
-  const int nitems = bwd_item_count(nblk), nslots = bwd_slot_count(nblk);
-  Item* items = (Item*)items_ws;
-  hipLaunchKernelGGL(bwd_items_kernel, dim3(1), dim3(1024), 0, st, nblk, items, slot_base);
+  const int NJ = s.B * s.Hkv * nblk;
+  Item* items = (Item*)ws.items;
+  hipLaunchKernelGGL(bwd_lists_kernel, dim3(nblk, s.Hkv, s.B), dim3(256), 0, st, s, revmap, ws.lists,
+                     ws.counts);
+  hipLaunchKernelGGL(bwd_items_kernel, dim3(1), dim3(1024), 0, st, NJ, nblk, s.G, ws.counts, items,
+                     ws.slot_base, ws.slot_cnt, ws.nitems);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int grid_items = bwd_item_bound(s);
   if (is_bf16) {
     if (s.D == 64)
-      e = launch_kv_g<bf16, 64>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
+      e = launch_kv_g<bf16, 64>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
     else
-      e = launch_kv_g<bf16, 128>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
+      e = launch_kv_g<bf16, 128>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
   } else {
-    e = launch_kv_g<float, 64>(s, items, nitems, nslots, q, bimg, lse, delta, dos, revmap, dk, dv, part, st);
+    e = launch_kv_g<float, 64>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
   }
   if (e != hipSuccess) return e;
-  if (nslots == 0) return hipSuccess;
-  dim3 grid(nblk, s.Hkv, s.B);
   if (is_bf16) {
     if (s.D == 64)
-      hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 64>), grid, dim3(256), 0, st, s, slot_base, part,
-                         nslots, (bf16*)dk, (bf16*)dv);
+      hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 64>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
+                         ws.slot_cnt, ws.part, (bf16*)dk, (bf16*)dv);
     else
-      hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 128>), grid, dim3(256), 0, st, s, slot_base, part,
-                         nslots, (bf16*)dk, (bf16*)dv);
+      hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 128>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
+                         ws.slot_cnt, ws.part, (bf16*)dk, (bf16*)dv);
   } else {
-    hipLaunchKernelGGL((bwd_reduce_kernel<float, 64>), grid, dim3(256), 0, st, s, slot_base, part,
-                       nslots, (float*)dk, (float*)dv);
+    hipLaunchKernelGGL((bwd_reduce_kernel<float, 64>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
+                       ws.slot_cnt, ws.part, (float*)dk, (float*)dv);
   }
   return hipGetLastError();
 }
 
-size_t bwd_items_bytes(int nblk) { return (size_t)bwd_item_count(nblk) * sizeof(Item); }
-size_t bwd_part_floats(const Shape& s) {
-  return (size_t)s.B * s.Hkv * bwd_slot_count(s.T / kBlock) * 2 * kBlock * s.D;
-}
+size_t bwd_items_bytes(const Shape& s) { return (size_t)bwd_item_bound(s) * sizeof(Item); }
+size_t bwd_part_floats(const Shape& s) { return (size_t)bwd_item_bound(s) * 2 * kBlock * s.D; }
 
 }  // namespace nsa

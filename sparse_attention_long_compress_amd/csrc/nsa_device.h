@@ -125,6 +125,17 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
   return o;
 }
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+// Store 8 consecutive fp32 values (16-byte aligned source) as T.
+__device__ __forceinline__ void store8(bf16* p, const float* x) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x), b = *reinterpret_cast<const f32x4*>(x + 4);
+  bf16x8 r;
+  for (int i = 0; i < 4; ++i) { r[i] = (bf16)a[i]; r[4 + i] = (bf16)b[i]; }
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+  reinterpret_cast<f32x4*>(p)[0] = *reinterpret_cast<const f32x4*>(x);
+  reinterpret_cast<f32x4*>(p)[1] = *reinterpret_cast<const f32x4*>(x + 4);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

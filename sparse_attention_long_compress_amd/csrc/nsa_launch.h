@@ -48,11 +48,24 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
 hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
                          const int32_t* indices, const float* lse, const float* delta,
                          const void* dos, void* dq, hipStream_t st);
+// Planning and partial-sum buffers of the dk/dv pass (all in the workspace):
+//   lists [B][Hkv][nblk][T] u16 positions that selected each block, counts
+//   [B][Hkv][nblk], items (bwd_items_bytes), slot_base / slot_cnt
+//   [B][Hkv][nblk], nitems (1 int), part (bwd_part_floats fp32).
+struct BwdPlanWs {
+  void* items;
+  uint16_t* lists;
+  int* counts;
+  int* slot_base;
+  int* slot_cnt;
+  int* nitems;
+  float* part;
+};
 hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* bimg,
                            const float* lse, const float* delta, const void* dos,
-                           const uint64_t* revmap, void* dk, void* dv, void* items_ws,
-                           int* slot_base, float* part, hipStream_t st);
-size_t bwd_items_bytes(int nblk);
+                           const uint64_t* revmap, void* dk, void* dv, const BwdPlanWs& ws,
+                           hipStream_t st);
+size_t bwd_items_bytes(const Shape& s);
 size_t bwd_part_floats(const Shape& s);
 
 }  // namespace nsa
