@@ -487,6 +487,267 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
   }
 }
 
+// ------------------------------------------------------------------ B3, paired waves
+// bf16 at head_dim 64: eight waves, two per SIMD.  Waves w and w + 4 form pair
+// p = w % 4 (same SIMD) and split the block's keys: wave half kh = w / 4 owns
+// the 16-key subtiles 2 kh and 2 kh + 1 (dK, dV accumulators: 64 fp32 per
+// lane).  Pair p takes chunks p, p + 4, ... (one per round); its two waves
+// stage each chunk together (q + lse | Delta by the first, dOs by the second)
+// into the pair's LDS ring, and one workgroup barrier per round publishes the
+// round's chunks and frees the previous round's stages.
+template <typename T, int D, int G>
+struct KvPairCfg {
+  typedef BwdImage<T, D> Img;
+  static constexpr int NW = 8, NT = NW * 64, NP = 4;   // waves, pairs
+  static constexpr int CR = 32, CP = CR / G;
+  static constexpr int ES = sizeof(T);
+  static constexpr int ROWB = D * ES, SLOTS = ROWB / 16, TB = CR * ROWB;
+  static constexpr int NLD = TB / 1024, RPI = 1024 / ROWB;
+  static constexpr int STAGE = 2 * TB + 256;
+  static constexpr int NR = 3;                          // ring stages per pair
+  static constexpr int L0 = NLD + 1, L1 = NLD;          // loads per chunk of key halves 0 and 1
+  static constexpr int NFRAG = Img::NFRAG, NV = Img::NV;
+  static constexpr int FRAG_BYTES = NV * 1024;
+  static constexpr int KVB = 2 * NFRAG * FRAG_BYTES;
+  static constexpr int KS = D / 32, MT = D / 16;
+  static constexpr int NFW = 2 * MT;                    // accumulator fragments per tensor and wave
+  static constexpr int NFR = 4 * MT;                    // accumulator fragments per tensor and block
+  static constexpr int MAXPOS = kMaxItemPos;
+  static constexpr size_t RING = (size_t)NP * NR * STAGE;
+  static constexpr size_t LDS = KVB + RING + MAXPOS * 2;
+  static_assert(CP >= 1 && CP * G == CR, "a chunk holds whole positions");
+  static_assert(RING >= (size_t)NW * NFW * 1024 && RING >= (size_t)kBlock * D * 4, "reduction fits in the ring");
+  static_assert((NR - 2) * L0 < 64, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel(
+    Shape s, const Item* __restrict__ items, const T* __restrict__ q,
+    const unsigned char* __restrict__ bimg, const float* __restrict__ lse,
+    const float* __restrict__ delta, const T* __restrict__ dos, const uint16_t* __restrict__ lists,
+    const int* __restrict__ nitems, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ part) {
+  typedef KvPairCfg<T, D, G> C;
+  constexpr int NT = C::NT, NP = C::NP, CP = C::CP, TB = C::TB, NLD = C::NLD, RPI = C::RPI;
+  constexpr int SLOTS = C::SLOTS, STAGE = C::STAGE, NR = C::NR, L0 = C::L0, L1 = C::L1;
+  constexpr int NFRAG = C::NFRAG, FRAG_BYTES = C::FRAG_BYTES, KVB = C::KVB;
+  constexpr int KS = C::KS, MT = C::MT, NFW = C::NFW, NFR = C::NFR, ROWB = C::ROWB;
+  typedef typename Frag<T>::type FragT;
+  typedef typename BwdImage<T, D>::K KI;
+  const float INF = __builtin_inff();
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* kv = smem;                                        // [KVB]
+  unsigned char* ring = smem + KVB;                                // [NP][NR][STAGE]
+  uint16_t* plist = reinterpret_cast<uint16_t*>(ring + C::RING);  // [MAXPOS]
+
+  if ((int)blockIdx.x >= *nitems) return;
+  const Item it = items[blockIdx.x];
+  const int nblk = s.T / kBlock;
+  const int g = it.bg % s.Hkv, b = it.bg / s.Hkv;
+  const int j = it.j;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int pr = w % NP, kh = w / NP;
+  const int l = threadIdx.x % kWave;
+  const int a = l >> 4, col = l & 15;
+  const float c1 = s.scale * kLog2e;
+  const size_t q_row = (size_t)s.Hq * D;
+
+  {
+    const unsigned char* src = bimg + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES + 16 * l;
+    for (int pc = w; pc < KVB / 1024; pc += C::NW)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024), (void*)(kv + (size_t)pc * 1024),
+                                       16, 0, 0);
+  }
+  const int npos = it.hi - it.lo;
+  {
+    const uint16_t* src = lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
+    for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  f32x4 adk[NFW], adv[NFW];
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) { adk[i] = zero4(); adv[i] = zero4(); }
+
+  const int nch = (npos + CP - 1) / CP;
+  const int rounds = (nch + NP - 1) / NP;
+  const int last_key_mask = j * kBlock + kBlock - 1;
+  unsigned char* pring = ring + (size_t)pr * NR * STAGE;
+  auto has = [&](int r) { return r * NP + pr < nch; };
+
+  // this wave's share of the loads of its pair's chunk of round r
+  auto issue = [&](int r) {
+    if (!has(r)) return;
+    const int ck = r * NP + pr;
+    unsigned char* st = pring + (size_t)(r % NR) * STAGE;
+    const T* src_t = kh == 0 ? q : dos;
+    unsigned char* dst_t = st + (kh == 0 ? 0 : TB);
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int R = n * RPI + l / SLOTS, sl = l % SLOTS;
+      const int qi = ck * CP + R / G;
+      const int t = plist[qi < npos ? qi : 0];
+      const int h = g * G + R % G;
+      const int c = (sl & ~7) | ((sl & 7) ^ row_swz(R));
+      const size_t off = ((size_t)b * s.T + t) * q_row + (size_t)h * D + c * (16 / sizeof(T));
+      __builtin_amdgcn_global_load_lds((const void*)(src_t + off), (void*)(dst_t + n * 1024), 16, 0, 0);
+    }
+    if (kh == 0) {
+      const int R = l & 31;
+      const int qi = ck * CP + R / G;
+      const int t = plist[qi < npos ? qi : 0];
+      const int h = g * G + R % G;
+      const float* src = (l < 32 ? lse : delta) + ((size_t)b * s.Hq + h) * s.T + t;
+      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(st + 2 * TB), 4, 0, 0);
+    }
+  };
+
+  for (int r = 0; r < NR - 1; ++r) issue(r);
+  for (int r = 0; r < rounds; ++r) {
+    // this wave's loads of round r are done when at most the later rounds' remain
+    if (has(r + NR - 2)) {
+      if (kh == 0) wait_vmcnt<(NR - 2) * L0>();
+      else wait_vmcnt<(NR - 2) * L1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_loads();  // round r's chunks are in LDS; round r-1's stages are free
+    issue(r + NR - 1);
+    if (!has(r)) continue;
+    const int ck = r * NP + pr;
+    const unsigned char* st = pring + (size_t)(r % NR) * STAGE;
+    const unsigned char* qs = st;
+    const unsigned char* ds = st + TB;
+    const float* meta = reinterpret_cast<const float*>(st + 2 * TB);
+
+    float lr[8], dl[8];
+    {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(meta + 8 * a);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(meta + 8 * a + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(meta + 32 + 8 * a);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(meta + 32 + 8 * a + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lr[e] = l0[e] * kLog2e;
+        lr[4 + e] = l1[e] * kLog2e;
+        dl[e] = d0[e];
+        dl[4 + e] = d1[e];
+      }
+    }
+    if ((ck + 1) * CP > npos) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ck * CP + (8 * a + e) / G >= npos) lr[e] = INF;
+    }
+    const bool masked = __builtin_amdgcn_readfirstlane(plist[ck * CP]) < last_key_mask;
+
+    FragT qa[2][KS], da[2][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int R = 8 * (col >> 2) + 4 * u + (col & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qa[u][ks] = row_frag<T, ROWB>(qs, R, ks * 32 + 8 * a);
+        da[u][ks] = row_frag<T, ROWB>(ds, R, ks * 32 + 8 * a);
+      }
+    }
+    FragT pf[2], sf[2];
+#pragma unroll
+    for (int vv = 0; vv < 2; ++vv) {
+      const int v = 2 * kh + vv;
+      f32x4 sv[2] = {zero4(), zero4()}, dp[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const FragT kf = lds_frag<T>(kv + (size_t)(4 * ks + v) * FRAG_BYTES, l);
+        const FragT vf = lds_frag<T>(kv + (size_t)(NFRAG + 4 * ks + v) * FRAG_BYTES, l);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          sv[u] = mma(sv[u], qa[u][ks], kf);
+          dp[u] = mma(dp[u], da[u][ks], vf);
+        }
+      }
+      float p[8], x[8];
+      if (!masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]);
+          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+        }
+      } else {
+        const int key = j * kBlock + KI::krow(v, col);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int qi = ck * CP + (8 * a + e) / G;
+          const int t = plist[qi < npos ? qi : 0];
+          p[e] = key <= t ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
+          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+        }
+      }
+      pf[vv] = Frag<T>::from_f32(p);
+      sf[vv] = Frag<T>::from_f32(x);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const FragT dt = col_frag<T, ROWB>(ds, l, m);
+      const FragT qt = col_frag<T, ROWB>(qs, l, m);
+#pragma unroll
+      for (int vv = 0; vv < 2; ++vv) {
+        adv[vv * MT + m] = mma(adv[vv * MT + m], pf[vv], dt);
+        adk[vv * MT + m] = mma(adk[vv * MT + m], sf[vv], qt);
+      }
+    }
+  }
+
+  // sum the four pairs' accumulators through LDS and write (as the 4-wave kernel)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(ring);
+  const size_t k_row = (size_t)s.Hkv * D;
+#pragma unroll
+  for (int tns = 0; tns < 2; ++tns) {
+#pragma unroll
+    for (int fi = 0; fi < NFW; ++fi)
+      *reinterpret_cast<f32x4*>(red + ((size_t)(w * NFW + fi) * 64 + l) * 4) = tns == 0 ? adk[fi] : adv[fi];
+    __syncthreads();
+    // output fragment of = w, w + 8 (of NFR): key half kh2 = of / NFW, local fragment fl = of % NFW
+    f32x4 sum[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int of = w + o * C::NW;
+      const int kh2 = of / NFW, fl = of % NFW;
+      sum[o] = zero4();
+      for (int p2 = 0; p2 < NP; ++p2)
+        sum[o] += *reinterpret_cast<const f32x4*>(red + ((size_t)((kh2 * NP + p2) * NFW + fl) * 64 + l) * 4);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int of = w + o * C::NW;
+      const int kh2 = of / NFW, fl = of % NFW;
+      const int v = 2 * kh2 + fl / MT, m = fl % MT;
+      const int fi = v * MT + m;  // fragment index of the 4-wave kernel's partial layout
+      if (it.slot >= 0) {
+        float* ps = part + ((size_t)it.slot * 2 + tns) * (size_t)NFR * 256;
+        *reinterpret_cast<f32x4*>(ps + ((size_t)fi * 64 + l) * 4) = sum[o];
+      } else {
+        const float sc = tns == 0 ? s.scale : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[KI::krow(v, 4 * a + r) * D + 16 * m + col] = sum[o][r] * sc;
+      }
+    }
+    if (it.slot < 0) {
+      __syncthreads();
+      T* dst = (tns == 0 ? dk : dv) + ((size_t)b * s.T + j * kBlock) * k_row + (size_t)g * D;
+      for (int i = threadIdx.x; i < kBlock * D / 8; i += NT) {
+        const int kk = i / (D / 8), c8 = (i % (D / 8)) * 8;
+        store8(dst + (size_t)kk * k_row + c8, red + kk * D + c8);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ B4
 // grid (B Hkv nblk): the partial sums of a block's items, added in item order,
 // rows staged in LDS for 16-byte stores.
@@ -549,6 +810,21 @@ static hipError_t launch_kv_t(const Shape& s, const Item* items, int grid_items,
                      (T*)dk, (T*)dv, part);
   return hipGetLastError();
 }
+template <int G>
+static hipError_t launch_kv_pair(const Shape& s, const Item* items, int grid_items, const int* nitems,
+                                 const void* q, const void* bimg, const float* lse, const float* delta,
+                                 const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+                                 hipStream_t st) {
+  typedef KvPairCfg<bf16, 64, G> C;
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_pair_kernel<bf16, 64, G>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<bf16, 64, G>), dim3(grid_items), dim3(C::NT), C::LDS, st, s,
+                     items, (const bf16*)q, (const unsigned char*)bimg, lse, delta, (const bf16*)dos, lists,
+                     nitems, (bf16*)dk, (bf16*)dv, part);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_kv_g(const Shape& s, const Item* items, int grid_items, const int* nitems,
                               const void* q, const void* bimg, const float* lse, const float* delta,
@@ -580,8 +856,17 @@ hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const vo
   if (e != hipSuccess) return e;
   const int grid_items = bwd_item_bound(s);
   if (is_bf16) {
-    if (s.D == 64)
-      e = launch_kv_g<bf16, 64>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
+    if (s.D == 64) {
+#define NSA_KVP(GG) launch_kv_pair<GG>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st)
+      switch (s.G) {
+        case 1: e = NSA_KVP(1); break;
+        case 2: e = NSA_KVP(2); break;
+        case 4: e = NSA_KVP(4); break;
+        case 8: e = NSA_KVP(8); break;
+        default: e = NSA_KVP(16); break;
+      }
+#undef NSA_KVP
+    }
     else
       e = launch_kv_g<bf16, 128>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
   } else {
