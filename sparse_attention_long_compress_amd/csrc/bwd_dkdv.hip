@@ -257,6 +257,20 @@ __device__ __forceinline__ f32x8 col_frag<float, 256>(const unsigned char* base,
   return r;
 }
 
+// B fragment (32 rows x 16 channels, bf16) by two transposing reads at the
+// precomputed lane offsets of its two 4-row halves
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* base, const int (&off)[2]) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) unsigned char*)(base + off[0])));
+  const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) unsigned char*)(base + off[1])));
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  const s16x8 r = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 template <typename T, int D, int G>
@@ -504,7 +518,7 @@ struct KvPairCfg {
   static constexpr int ROWB = D * ES, SLOTS = ROWB / 16, TB = CR * ROWB;
   static constexpr int NLD = TB / 1024, RPI = 1024 / ROWB;
   static constexpr int STAGE = 2 * TB + 256;
-  static constexpr int NR = 3;                          // ring stages per pair
+  static constexpr int NR = 4;                          // ring stages per pair
   static constexpr int L0 = NLD + 1, L1 = NLD;          // loads per chunk of key halves 0 and 1
   static constexpr int NFRAG = Img::NFRAG, NV = Img::NV;
   static constexpr int FRAG_BYTES = NV * 1024;
@@ -577,30 +591,52 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
   unsigned char* pring = ring + (size_t)pr * NR * STAGE;
   auto has = [&](int r) { return r * NP + pr < nch; };
 
+  // lane-constant byte offsets inside a staged chunk (row-major, swizzled):
+  // A fragments of the row subtiles, transposing reads of the 16-channel tiles
+  static_assert(ROWB == 128, "paired kernel: bf16, head_dim 64");
+  auto slot_off = [](int R, int c) { return R * 128 + ((c ^ row_swz(R)) << 4); };
+  int roff[2][KS], troff[MT][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[u][ks] = slot_off(8 * (col >> 2) + 4 * u + (col & 3), ks * 4 + a);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      troff[m][hh] = slot_off(8 * a + 4 * hh + (col >> 2), 2 * m + ((col & 3) >> 1)) + ((col & 1) << 3);
+  // staging: per 1 KB load n, this lane's row (position index in the chunk,
+  // head) and the byte offset of its 16 bytes inside the (position, group) rows
+  int ld_pi[NLD], ld_off[NLD];
+#pragma unroll
+  for (int n = 0; n < NLD; ++n) {
+    const int R = n * RPI + l / SLOTS, sl = l % SLOTS;
+    ld_pi[n] = R / G;
+    ld_off[n] = ((R % G) * D + ((sl & ~7) | ((sl & 7) ^ row_swz(R))) * (16 / (int)sizeof(T))) * (int)sizeof(T);
+  }
+  const int mt_pi = (l & 31) / G;
+  const float* mt_src = (l < 32 ? lse : delta) + ((size_t)b * s.Hq + g * G + (l & 31) % G) * s.T;
+  const unsigned char* grp_q = (const unsigned char*)(q + (size_t)b * s.T * q_row + (size_t)g * G * D);
+  const unsigned char* grp_d = (const unsigned char*)(dos + (size_t)b * s.T * q_row + (size_t)g * G * D);
+
   // this wave's share of the loads of its pair's chunk of round r
   auto issue = [&](int r) {
     if (!has(r)) return;
     const int ck = r * NP + pr;
     unsigned char* st = pring + (size_t)(r % NR) * STAGE;
-    const T* src_t = kh == 0 ? q : dos;
+    const unsigned char* src_t = kh == 0 ? grp_q : grp_d;
     unsigned char* dst_t = st + (kh == 0 ? 0 : TB);
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int R = n * RPI + l / SLOTS, sl = l % SLOTS;
-      const int qi = ck * CP + R / G;
+      const int qi = ck * CP + ld_pi[n];
       const int t = plist[qi < npos ? qi : 0];
-      const int h = g * G + R % G;
-      const int c = (sl & ~7) | ((sl & 7) ^ row_swz(R));
-      const size_t off = ((size_t)b * s.T + t) * q_row + (size_t)h * D + c * (16 / sizeof(T));
-      __builtin_amdgcn_global_load_lds((const void*)(src_t + off), (void*)(dst_t + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src_t + (size_t)t * (q_row * sizeof(T)) + ld_off[n]),
+                                       (void*)(dst_t + n * 1024), 16, 0, 0);
     }
     if (kh == 0) {
-      const int R = l & 31;
-      const int qi = ck * CP + R / G;
+      const int qi = ck * CP + mt_pi;
       const int t = plist[qi < npos ? qi : 0];
-      const int h = g * G + R % G;
-      const float* src = (l < 32 ? lse : delta) + ((size_t)b * s.Hq + h) * s.T + t;
-      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(st + 2 * TB), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(mt_src + t), (void*)(st + 2 * TB), 4, 0, 0);
     }
   };
 
@@ -645,14 +681,12 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
 
     FragT qa[2][KS], da[2][KS];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int R = 8 * (col >> 2) + 4 * u + (col & 3);
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qa[u][ks] = row_frag<T, ROWB>(qs, R, ks * 32 + 8 * a);
-        da[u][ks] = row_frag<T, ROWB>(ds, R, ks * 32 + 8 * a);
+        qa[u][ks] = *reinterpret_cast<const FragT*>(qs + roff[u][ks]);
+        da[u][ks] = *reinterpret_cast<const FragT*>(ds + roff[u][ks]);
       }
-    }
     FragT pf[2], sf[2];
 #pragma unroll
     for (int vv = 0; vv < 2; ++vv) {
@@ -690,8 +724,8 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const FragT dt = col_frag<T, ROWB>(ds, l, m);
-      const FragT qt = col_frag<T, ROWB>(qs, l, m);
+      const FragT dt = tr_frag(ds, troff[m]);
+      const FragT qt = tr_frag(qs, troff[m]);
 #pragma unroll
       for (int vv = 0; vv < 2; ++vv) {
         adv[vv * MT + m] = mma(adv[vv * MT + m], pf[vv], dt);
