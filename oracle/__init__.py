@@ -67,13 +67,17 @@ def _load():
         lib.nsa_oracle_pool.argtypes = [ci, ci, ci, ci, ci, dp, dp]
         lib.nsa_oracle_pool.restype = ci
         lib.nsa_oracle_forward.argtypes = (
-            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [dp] * 5 + [ip, ci, dp, dp, ip, ci, ci]
+            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [dp] * 7 + [ip, ci, dp, dp, ip, ci, ci]
         )
         lib.nsa_oracle_forward.restype = ci
         lib.nsa_oracle_select_bwd.argtypes = (
             [ci] * 7 + [ctypes.c_double] + [dp] * 4 + [ip, dp, dp, dp, dp, ci]
         )
         lib.nsa_oracle_select_bwd.restype = ci
+        lib.nsa_oracle_backward.argtypes = (
+            [ci] * 8 + [ctypes.c_double] + [dp] * 4 + [ip, dp, dp, dp, dp, dp, ci]
+        )
+        lib.nsa_oracle_backward.restype = ci
         _lib = lib
     return _lib
 
@@ -107,7 +111,8 @@ def pool(x, blk: int = 64):
 def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: float | None = None,
             indices=None, want_scores: bool = False, rows=None, threads: int | None = None):
     """Full NSA forward.  Returns a dict of float64/int32 numpy arrays:
-    out, o_cmp, o_sel, o_win [B,T,Hq,D]; lse_sel [B,Hq,T]; indices [B,Hkv,T,top_k];
+    out, o_cmp, o_sel, o_win [B,T,Hq,D]; lse_sel, lse_win, lse_cmp [B,Hq,T] (lse_cmp
+    is -inf where no compressed block is visible); indices [B,Hkv,T,top_k];
     gap [B,Hkv,T]; scores [B,Hkv,T,nblk] (when want_scores).
 
     ``indices`` (optional, int32) freezes the selection to a table the oracle
@@ -125,6 +130,8 @@ def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: fl
         "o_sel": np.zeros((B, T, Hq, D)),
         "o_win": np.zeros((B, T, Hq, D)),
         "lse_sel": np.zeros((B, Hq, T)),
+        "lse_win": np.zeros((B, Hq, T)),
+        "lse_cmp": np.zeros((B, Hq, T)),
         "gap": np.zeros((B, Hkv, T)),
     }
     if indices is not None:
@@ -139,7 +146,8 @@ def forward(q, k, v, gates, *, top_k: int, window: int, blk: int = 64, scale: fl
         B, T, Hq, Hkv, D, blk, top_k, window, float(scale),
         _dptr(q), _dptr(k), _dptr(v), _dptr(gates),
         _dptr(res["out"]), _dptr(res["o_cmp"]), _dptr(res["o_sel"]), _dptr(res["o_win"]),
-        _dptr(res["lse_sel"]), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        _dptr(res["lse_sel"]), _dptr(res["lse_win"]), _dptr(res["lse_cmp"]),
+        idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
         1 if indices is not None else 0, _dptr(scores), _dptr(res["gap"]),
         rows_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if rows_a is not None
         else ctypes.POINTER(ctypes.c_int32)(), 0 if rows_a is None else len(rows_a),
@@ -174,3 +182,30 @@ def select_bwd(q, k, v, gates, indices, dout, *, top_k: int, blk: int = 64,
     if rc != 0:
         raise ValueError(f"nsa_oracle_select_bwd failed: {rc}")
     return dq, dk, dv
+
+
+def backward(q, k, v, gates, indices, dout, *, top_k: int, window: int, blk: int = 64,
+             scale: float | None = None, threads: int | None = None):
+    """Gradient of the whole NSA output (all three branches and the gates;
+    the selection frozen to ``indices``).  Returns (dq [B,T,Hq,D], dk, dv
+    [B,T,Hkv,D], dgates [B,T,Hq,3]) in float64."""
+    q, k, v, gates, dout = _f64(q), _f64(k), _f64(v), _f64(gates), _f64(dout)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    idx = np.ascontiguousarray(np.asarray(indices, dtype=np.int32))
+    assert idx.shape == (B, Hkv, T, top_k)
+    dq = np.zeros((B, T, Hq, D))
+    dk = np.zeros((B, T, Hkv, D))
+    dv = np.zeros((B, T, Hkv, D))
+    dg = np.zeros((B, T, Hq, 3))
+    rc = _load().nsa_oracle_backward(
+        B, T, Hq, Hkv, D, blk, top_k, window, float(scale),
+        _dptr(q), _dptr(k), _dptr(v), _dptr(gates),
+        idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _dptr(dout),
+        _dptr(dq), _dptr(dk), _dptr(dv), _dptr(dg),
+        threads if threads is not None else default_threads())
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_backward failed: {rc}")
+    return dq, dk, dv, dg

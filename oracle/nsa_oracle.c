@@ -26,7 +26,9 @@
  *   q, out, o_cmp, o_sel, o_win, dq : [B][T][Hq][D]
  *   k, v, dk, dv                    : [B][T][Hkv][D]
  *   gates                           : [B][T][Hq][3]  (cmp, sel, win)
- *   lse_sel                         : [B][Hq][T]
+ *   lse_sel, lse_win, lse_cmp       : [B][Hq][T]  (lse_cmp = -inf where no
+ *                                     compressed block is visible)
+ *   dgates                          : [B][T][Hq][3]
  *   indices                         : [B][Hkv][T][top_k]  ascending, -1 pad
  *   scores (nullable)               : [B][Hkv][T][nblk]   nblk = ceil(T/blk)
  *   gap (nullable)                  : [B][Hkv][T]
@@ -158,9 +160,9 @@ static int select_blocks(const oparams* p, int t, const double* S, int* out, dou
 int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k, int window,
                        double scale, const double* q, const double* k, const double* v,
                        const double* gates, double* out, double* o_cmp, double* o_sel,
-                       double* o_win, double* lse_sel, int32_t* indices, int indices_in,
-                       double* scores, double* gap, const int32_t* rows, int nrows,
-                       int nthreads) {
+                       double* o_win, double* lse_sel, double* lse_win, double* lse_cmp,
+                       int32_t* indices, int indices_in, double* scores, double* gap,
+                       const int32_t* rows, int nrows, int nthreads) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || blk < 1 || Hq % Hkv) return -2;
   if (top_k < 2 || window < 1) return -2;
   oparams p = {B, T, Hq, Hkv, D, blk, top_k, window, scale};
@@ -221,6 +223,7 @@ int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k,
                 }
                 double l = 0.0;
                 for (int j = 0; j < ncv; ++j) { prh[j] = exp(prh[j] - m); l += prh[j]; }
+                if (lse_cmp) lse_cmp[((size_t)b * Hq + h) * T + t] = m + log(l);
                 for (int j = 0; j < ncv; ++j) {
                   prh[j] /= l;
                   const double* vcj = vc + (((size_t)b * nc_all + j) * Hkv + g) * D;
@@ -228,6 +231,7 @@ int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k,
                   S[j] += prh[j];
                 }
               }
+              if (lse_cmp && ncv == 0) lse_cmp[((size_t)b * Hq + h) * T + t] = -INFINITY;
               if (o_cmp)
                 for (int d = 0; d < D; ++d) o_cmp[qidx(&p, b, t, h, d)] = oc[d];
               if (out)
@@ -267,7 +271,8 @@ int nsa_oracle_forward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k,
               if (lse_sel) lse_sel[((size_t)b * Hq + h) * T + t] = lse;
               int nw = 0;
               for (int s = w0; s <= t; ++s) wkeys[nw++] = s;
-              attend(&p, qv, k, v, b, g, wkeys, nw, ow, logit);
+              double lsw = attend(&p, qv, k, v, b, g, wkeys, nw, ow, logit);
+              if (lse_win) lse_win[((size_t)b * Hq + h) * T + t] = lsw;
               if (o_sel)
                 for (int d = 0; d < D; ++d) o_sel[qidx(&p, b, t, h, d)] = os[d];
               if (o_win)
@@ -366,5 +371,140 @@ int nsa_oracle_select_bwd(int B, int T, int Hq, int Hkv, int D, int blk, int top
       }
       free(keys); free(logit); free(os); free(dos);
     }
+  return err ? -1 : 0;
+}
+
+/* ---- Gradient of all three branches and of the gates ------------------------
+ * The selected blocks are held fixed (top-k is piecewise constant, so no
+ * gradient flows through the importance scores).  out = g_c o_cmp + g_s o_sel
+ * + g_w o_win, so
+ *   dgates[t,h] = (dout . o_cmp, dout . o_sel, dout . o_win)
+ * and each branch receives g_branch * dout.  Every branch is a softmax
+ * attention, so its gradient is the softmax Jacobian written out as in
+ * nsa_oracle_select_bwd, over its own keys:
+ *   selection : the tokens s <= t of the selected blocks;
+ *   window    : t - W < s <= t;
+ *   compression: the pooled keys Kc_j, Vc_j of the complete blocks with
+ *               64 (j + 1) - 1 <= t; their gradients dKc_j, dVc_j flow back
+ *               through the mean-pool as dk_s += dKc_j / blk, dv_s += dVc_j /
+ *               blk for the blk tokens s of block j ([DSA] COMPRESSION; [SIC]
+ *               Method: the pool is a plain mean).
+ * Scattered in query order, per (batch, KV group). */
+static void softmax_bwd(const oparams* p, int b, int g, const double* qv, const double* k,
+                        const double* v, const int* keys, int nkeys, const double* dob,
+                        double* dqv, double* dk, double* dv, double* logit, double* ob) {
+  int D = p->D;
+  double lse = attend(p, qv, k, v, b, g, keys, nkeys, ob, logit);
+  double delta = 0.0;
+  for (int d = 0; d < D; ++d) delta += dob[d] * ob[d];
+  for (int i = 0; i < nkeys; ++i) {
+    const double* kv = k + kidx(p, b, keys[i], g, 0);
+    const double* vv = v + kidx(p, b, keys[i], g, 0);
+    double P = exp(logit[i] - lse);
+    double dP = 0.0;
+    for (int d = 0; d < D; ++d) dP += dob[d] * vv[d];
+    double dS = P * (dP - delta);
+    double* dkv = dk + kidx(p, b, keys[i], g, 0);
+    double* dvv = dv + kidx(p, b, keys[i], g, 0);
+    for (int d = 0; d < D; ++d) {
+      dqv[d] += p->scale * dS * kv[d];
+      dkv[d] += p->scale * dS * qv[d];
+      dvv[d] += P * dob[d];
+    }
+  }
+}
+
+int nsa_oracle_backward(int B, int T, int Hq, int Hkv, int D, int blk, int top_k, int window,
+                        double scale, const double* q, const double* k, const double* v,
+                        const double* gates, const int32_t* indices, const double* dout,
+                        double* dq, double* dk, double* dv, double* dgates, int nthreads) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || blk < 1 || Hq % Hkv) return -2;
+  if (top_k < 1 || window < 1) return -2;
+  oparams p = {B, T, Hq, Hkv, D, blk, top_k, window, scale};
+  int G = Hq / Hkv;
+  int nc = T / blk;
+  /* pooled keys / values as [B][nc][Hkv][D]: the layout of k with T -> nc */
+  oparams pc = p;
+  pc.T = nc > 0 ? nc : 1;
+  double* kc = (double*)calloc((size_t)B * pc.T * Hkv * D, sizeof(double));
+  double* vc = (double*)calloc((size_t)B * pc.T * Hkv * D, sizeof(double));
+  double* dkc = (double*)calloc((size_t)B * pc.T * Hkv * D, sizeof(double));
+  double* dvc = (double*)calloc((size_t)B * pc.T * Hkv * D, sizeof(double));
+  if (!kc || !vc || !dkc || !dvc) { free(kc); free(vc); free(dkc); free(dvc); return -1; }
+  if (nc > 0) { pool(&p, k, kc); pool(&p, v, vc); }
+  memset(dq, 0, sizeof(double) * (size_t)B * T * Hq * D);
+  memset(dk, 0, sizeof(double) * (size_t)B * T * Hkv * D);
+  memset(dv, 0, sizeof(double) * (size_t)B * T * Hkv * D);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      int* keys = (int*)malloc(sizeof(int) * (size_t)(T + 1));
+      double* logit = (double*)malloc(sizeof(double) * (size_t)(T + 1));
+      double* ob = (double*)malloc(sizeof(double) * (size_t)D);
+      double* dob = (double*)malloc(sizeof(double) * (size_t)D);
+      if (!keys || !logit || !ob || !dob) {
+#pragma omp atomic write
+        err = 1;
+      } else {
+        for (int t = 0; t < T; ++t) {
+          const int32_t* irow = indices + (((size_t)b * Hkv + g) * T + t) * top_k;
+          for (int hh = 0; hh < G; ++hh) {
+            int h = g * G + hh;
+            const double* qv = q + qidx(&p, b, t, h, 0);
+            const double* dov = dout + qidx(&p, b, t, h, 0);
+            const double* gt = gates + (((size_t)b * T + t) * Hq + h) * 3;
+            double* dqv = dq + qidx(&p, b, t, h, 0);
+            double* dg = dgates + (((size_t)b * T + t) * Hq + h) * 3;
+            /* compression: pooled keys j with 64 (j + 1) - 1 <= t */
+            int ncv = (t + 1) / blk;
+            for (int j = 0; j < ncv; ++j) keys[j] = j;
+            for (int d = 0; d < D; ++d) dob[d] = gt[0] * dov[d];
+            if (ncv > 0) {
+              softmax_bwd(&pc, b, g, qv, kc, vc, keys, ncv, dob, dqv, dkc, dvc, logit, ob);
+            } else {
+              for (int d = 0; d < D; ++d) ob[d] = 0.0;
+            }
+            double s0 = 0.0;
+            for (int d = 0; d < D; ++d) s0 += dov[d] * ob[d];
+            dg[0] = s0;
+            /* selection */
+            int nk = 0;
+            for (int i = 0; i < top_k; ++i) {
+              int j = irow[i];
+              if (j < 0) continue;
+              for (int s = j * blk; s < (j + 1) * blk && s <= t && s < T; ++s) keys[nk++] = s;
+            }
+            for (int d = 0; d < D; ++d) dob[d] = gt[1] * dov[d];
+            softmax_bwd(&p, b, g, qv, k, v, keys, nk, dob, dqv, dk, dv, logit, ob);
+            double s1 = 0.0;
+            for (int d = 0; d < D; ++d) s1 += dov[d] * ob[d];
+            dg[1] = s1;
+            /* window */
+            int nw = 0;
+            for (int s = t - window + 1 > 0 ? t - window + 1 : 0; s <= t; ++s) keys[nw++] = s;
+            for (int d = 0; d < D; ++d) dob[d] = gt[2] * dov[d];
+            softmax_bwd(&p, b, g, qv, k, v, keys, nw, dob, dqv, dk, dv, logit, ob);
+            double s2 = 0.0;
+            for (int d = 0; d < D; ++d) s2 += dov[d] * ob[d];
+            dg[2] = s2;
+          }
+        }
+        /* the mean-pool's gradient: every token of block j gets dKc_j / blk */
+        for (int j = 0; j < nc; ++j)
+          for (int i = 0; i < blk; ++i)
+            for (int d = 0; d < D; ++d) {
+              dk[kidx(&p, b, j * blk + i, g, d)] += dkc[kidx(&pc, b, j, g, d)] / blk;
+              dv[kidx(&p, b, j * blk + i, g, d)] += dvc[kidx(&pc, b, j, g, d)] / blk;
+            }
+      }
+      free(keys); free(logit); free(ob); free(dob);
+    }
+  free(kc); free(vc); free(dkc); free(dvc);
   return err ? -1 : 0;
 }

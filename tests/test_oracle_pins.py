@@ -446,3 +446,98 @@ def test_row_subset_matches_full_run():
         np.testing.assert_array_equal(sub[name][:, rows], full[name][:, rows])
     np.testing.assert_array_equal(sub["indices"][:, :, rows], full["indices"][:, :, rows])
     np.testing.assert_array_equal(sub["lse_sel"][:, :, rows], full["lse_sel"][:, :, rows])
+
+
+# ------------------------------------------------------------------ full gradient
+def test_backward_central_finite_differences():
+    # d/dx of L = sum(dout * out) over all three branches and the gates, with the
+    # selection frozen; window 40 cuts blocks, top_k 2 leaves block 1 unselected
+    # for the last block's queries.
+    B, T, Hq, Hkv, D, topk, W = 1, 192, 2, 1, 4, 2, 40
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=41)
+    dout = np.random.default_rng(42).standard_normal(q.shape)
+    idx = oracle.forward(q, k, v, g, top_k=topk, window=W)["indices"]
+    dq, dk, dv, dg = oracle.backward(q, k, v, g, idx, dout, top_k=topk, window=W)
+
+    def loss(**kw):
+        a = {"q": q, "k": k, "v": v, "gates": g}
+        a.update(kw)
+        o = oracle.forward(a["q"], a["k"], a["v"], a["gates"], top_k=topk, window=W, indices=idx)
+        return float((dout * o["out"]).sum())
+
+    rng = np.random.default_rng(43)
+    h = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("gates", g, dg)):
+        for _ in range(8):
+            pos = tuple(rng.integers(0, s) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[pos] += h
+            am[pos] -= h
+            fd = (loss(**{name: ap}) - loss(**{name: am})) / (2 * h)
+            assert abs(fd - grad[pos]) < 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def _nsa_loss_torch(q, k, v, g, idx, dout, topk, W, scale, blk=64):
+    """Library pin: the three branches written with torch fp64 ops (avg_pool1d
+    for the compression, explicit boolean masks), differentiated by autograd."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    gt = torch.from_numpy(g).requires_grad_(True)
+    qh = qt.permute(0, 2, 1, 3)                                        # [B,Hq,T,D]
+    kh = kt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vh = vt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    t_ = np.arange(T)
+    blk_of = t_ // blk
+    # selection and window masks
+    msel = np.zeros((B, Hq, T, T), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(T):
+                sel = idx[b, h // G, t]
+                msel[b, h, t] = np.isin(blk_of, sel[sel >= 0]) & (t_ <= t)
+    mwin = (t_[None, :] <= t_[:, None]) & (t_[None, :] > t_[:, None] - W)
+    o_sel = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=torch.from_numpy(msel), scale=scale)
+    o_win = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=torch.from_numpy(mwin), scale=scale)
+    # compression: pooled keys over complete blocks, visible when 64 (j + 1) - 1 <= t
+    nc = T // blk
+    kc = F.avg_pool1d(kh.reshape(-1, T, D).transpose(1, 2), blk, blk).transpose(1, 2).reshape(B, Hq, nc, D)
+    vc = F.avg_pool1d(vh.reshape(-1, T, D).transpose(1, 2), blk, blk).transpose(1, 2).reshape(B, Hq, nc, D)
+    rows = np.arange(blk - 1, T)                                       # rows with a visible block
+    mcmp = (blk * (np.arange(nc)[None, :] + 1) - 1) <= rows[:, None]
+    o_rows = F.scaled_dot_product_attention(qh[:, :, rows], kc, vc, attn_mask=torch.from_numpy(mcmp),
+                                            scale=scale)
+    o_cmp = torch.zeros_like(o_sel)
+    o_cmp = o_cmp.index_copy(2, torch.from_numpy(rows), o_rows)
+    gh = gt.permute(0, 2, 1, 3)                                        # [B,Hq,T,3]
+    out = gh[..., 0:1] * o_cmp + gh[..., 1:2] * o_sel + gh[..., 2:3] * o_win
+    (out.permute(0, 2, 1, 3) * torch.from_numpy(dout)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(), gt.grad.numpy()
+
+
+def test_backward_matches_autograd_of_torch_branches():
+    B, T, Hq, Hkv, D, topk, W = 2, 320, 4, 2, 8, 3, 100
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=44)
+    dout = np.random.default_rng(45).standard_normal(q.shape)
+    idx = oracle.forward(q, k, v, g, top_k=topk, window=W)["indices"]
+    got = oracle.backward(q, k, v, g, idx, dout, top_k=topk, window=W)
+    want = _nsa_loss_torch(q, k, v, g, idx, dout, topk, W, 1 / np.sqrt(D))
+    for name, a, b_ in zip(("dq", "dk", "dv", "dgates"), got, want):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-11, err_msg=name)
+
+
+def test_backward_selection_part_equals_select_bwd():
+    # with the compression and window gates at zero only the selection gradient remains
+    B, T, Hq, Hkv, D, topk = 1, 256, 4, 2, 8, 3
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=46)
+    g[..., 0] = 0.0
+    g[..., 2] = 0.0
+    dout = np.random.default_rng(47).standard_normal(q.shape)
+    idx = oracle.forward(q, k, v, g, top_k=topk, window=30)["indices"]
+    dq, dk, dv, _ = oracle.backward(q, k, v, g, idx, dout, top_k=topk, window=30)
+    rq, rk, rv = oracle.select_bwd(q, k, v, g, idx, dout, top_k=topk)
+    for a, b_ in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-13)
