@@ -114,9 +114,10 @@ const char* nsa_status_string(nsa_status_t status);
  * Returns NSA_OK, NSA_ERR_SHAPE, NSA_ERR_DTYPE or NSA_ERR_UNSUPPORTED. */
 nsa_status_t nsa_check_params(const nsa_params_t* p);
 
-/* Bytes of device workspace needed by nsa_forward (for_backward = 0) or by
- * nsa_select_bwd (for_backward = 1).  Returns 0 for invalid params.  The size
- * is monotone in seq_len and batch. */
+/* Bytes of device workspace needed by nsa_forward / nsa_forward_train
+ * (for_backward = 0), by nsa_select_bwd (for_backward = 1) or by nsa_backward
+ * (for_backward = 2).  Returns 0 for invalid params.  The size is monotone in
+ * seq_len and batch. */
 size_t nsa_workspace_size(const nsa_params_t* p, int for_backward);
 
 /* Compression step alone ([DSA] COMPRESSION; [SIC] Method: mean-pool over
@@ -171,6 +172,58 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
                             const int32_t* indices, const float* lse_sel, const void* o_sel,
                             const void* dout, const nsa_params_t* p, void* dq, void* dk,
                             void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* Tensors the full backward reads, written by nsa_forward_train.  All device
+ * pointers, 16-byte aligned, owned by the caller:
+ *   indices          int32 [B][Hkv][T][top_k]  (output, or input with
+ *                    NSA_INDICES_IN)
+ *   lse_sel, lse_win, lse_cmp   fp32 [B][Hq][T]: log-sum-exp (natural log) of
+ *                    the selection, window and compressed softmaxes; lse_cmp
+ *                    is -inf where no compressed block is visible (t < 63)
+ *   o_sel, o_win, o_cmp         [B][T][Hq][D] in params->dtype: the UNGATED
+ *                    branch outputs (o_cmp is 0 for t < 63) */
+typedef struct {
+  int32_t* indices;
+  float* lse_sel;
+  float* lse_win;
+  float* lse_cmp;
+  void* o_sel;
+  void* o_win;
+  void* o_cmp;
+} nsa_saved_t;
+
+/* nsa_forward that also writes every tensor of `saved` (all seven required)
+ * for nsa_backward.  Same checks and the same `out` as nsa_forward.  flags:
+ * only NSA_INDICES_IN is allowed (training runs all three branches).
+ * workspace: at least nsa_workspace_size(p, 0) bytes. */
+nsa_status_t nsa_forward_train(const void* q, const void* k, const void* v, const void* gates,
+                               const nsa_params_t* p, void* out, const nsa_saved_t* saved,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Gradient of the whole NSA output ([DSA] How Does NSA Work?: the three
+ * branches and the gate mix; [SIC] Method: mean-pool compression), with the
+ * selection held fixed (top-k is piecewise constant; no gradient flows
+ * through the importance scores):
+ *   dgates[t,h] = (dout.o_cmp, dout.o_sel, dout.o_win)          [B][T][Hq][3]
+ *   dq, dk, dv  = the softmax-Jacobian gradients of the selection branch
+ *                 (tokens of the selected blocks, s <= t), the window branch
+ *                 (t - W < s <= t) and the compression branch (pooled keys of
+ *                 the complete blocks visible to t, whose gradients flow back
+ *                 through the mean-pool as 1/64 per token of the block),
+ *                 each branch receiving g_branch * dout.
+ * Same two-pass scheme as nsa_select_bwd (query-stationary dq, key-stationary
+ * dk/dv over per-block row lists, partial sums added in a fixed order): no
+ * atomics, bitwise reproducible.
+ *   saved : as written by nsa_forward_train for the same inputs (read only).
+ *   dout  : gradient of `out`.
+ *   dq [B][T][Hq][D], dk, dv [B][T][Hkv][D], dgates [B][T][Hq][3] in
+ *   params->dtype: outputs, overwritten.
+ * flags: only NSA_INDICES_IN may be set (ignored here).
+ * workspace: at least nsa_workspace_size(p, 2) bytes. */
+nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const void* gates,
+                          const nsa_saved_t* saved, const void* dout, const nsa_params_t* p,
+                          void* dq, void* dk, void* dv, void* dgates, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

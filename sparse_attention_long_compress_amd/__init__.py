@@ -20,11 +20,21 @@ SKIP_CMP_OUT, SKIP_SEL, SKIP_WIN, INDICES_IN = 1, 2, 4, 8
 EXPORTED = (
     "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_workspace_size",
     "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
+    "nsa_forward_train", "nsa_backward",
 )
 
 
 class NsaError(RuntimeError):
     pass
+
+
+class NsaSaved(ctypes.Structure):
+    """nsa_saved_t: the forward tensors the full backward reads."""
+    _fields_ = [
+        ("indices", ctypes.c_void_p), ("lse_sel", ctypes.c_void_p), ("lse_win", ctypes.c_void_p),
+        ("lse_cmp", ctypes.c_void_p), ("o_sel", ctypes.c_void_p), ("o_win", ctypes.c_void_p),
+        ("o_cmp", ctypes.c_void_p),
+    ]
 
 
 class NsaParams(ctypes.Structure):
@@ -68,6 +78,11 @@ def lib():
         L.nsa_select_bwd.argtypes = [vp, vp, vp, vp, i32p, f32p, vp, vp, P, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
         L.nsa_select_bwd.restype = ctypes.c_int
+        S = ctypes.POINTER(NsaSaved)
+        L.nsa_forward_train.argtypes = [vp, vp, vp, vp, P, vp, S, vp, ctypes.c_size_t, vp]
+        L.nsa_forward_train.restype = ctypes.c_int
+        L.nsa_backward.argtypes = [vp, vp, vp, vp, S, vp, P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.nsa_backward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -121,11 +136,13 @@ def params_for(q, k, *, top_k, window, scale=None, flags=0):
                        scale=scale, flags=flags)
 
 
-def workspace_size(p: NsaParams, backward: bool = False) -> int:
-    return int(lib().nsa_workspace_size(ctypes.byref(p), 1 if backward else 0))
+def workspace_size(p: NsaParams, backward=False) -> int:
+    """backward: False (forward), True (selection backward) or "full" (nsa_backward)."""
+    mode = 2 if backward == "full" else (1 if backward else 0)
+    return int(lib().nsa_workspace_size(ctypes.byref(p), mode))
 
 
-def alloc_workspace(p: NsaParams, device, backward: bool = False):
+def alloc_workspace(p: NsaParams, device, backward=False):
     torch = _torch()
     n = workspace_size(p, backward)
     if n == 0:
@@ -217,3 +234,53 @@ def select_bwd(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, scale=No
                                 _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
            "nsa_select_bwd")
     return dq, dk, dv
+
+
+SAVED = ("indices", "lse_sel", "lse_win", "lse_cmp", "o_sel", "o_win", "o_cmp")
+
+
+def _saved_struct(saved):
+    return NsaSaved(*[_ptr(saved[n]) for n in SAVED])
+
+
+def forward_train(q, k, v, gates, *, top_k, window, scale=None, indices=None, out=None,
+                  workspace=None, stream=None):
+    """NSA forward that also returns every tensor the full backward needs
+    (nsa_forward_train): a dict with 'out' and the keys of SAVED."""
+    torch = _torch()
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    flags = INDICES_IN if indices is not None else 0
+    p = params_for(q, k, top_k=top_k, window=window, scale=scale, flags=flags)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device)
+    res = {"out": out if out is not None else torch.empty_like(q)}
+    res["indices"] = indices if indices is not None else torch.empty(
+        (B, Hkv, T, top_k), dtype=torch.int32, device=q.device)
+    for n in ("lse_sel", "lse_win", "lse_cmp"):
+        res[n] = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    for n in ("o_sel", "o_win", "o_cmp"):
+        res[n] = torch.empty_like(q)
+    sv = _saved_struct(res)
+    _check(lib().nsa_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), ctypes.byref(p),
+                                   _ptr(res["out"]), ctypes.byref(sv), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "nsa_forward_train")
+    return res
+
+
+def backward(q, k, v, gates, saved, dout, *, top_k, window, scale=None, workspace=None,
+             stream=None, out=None):
+    """(dq, dk, dv, dgates) of the whole NSA output (nsa_backward); ``saved`` is
+    the dict forward_train returned; ``out`` may pass preallocated tensors."""
+    torch = _torch()
+    p = params_for(q, k, top_k=top_k, window=window, scale=scale)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device, backward="full")
+    if out is not None:
+        dq, dk, dv, dg = out
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dg = torch.empty_like(gates)
+    sv = _saved_struct(saved)
+    _check(lib().nsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), ctypes.byref(sv), _ptr(dout),
+                              ctypes.byref(p), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws),
+                              ws.numel(), _stream(stream)), "nsa_backward")
+    return dq, dk, dv, dg

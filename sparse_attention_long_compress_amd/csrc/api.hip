@@ -71,27 +71,55 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
   return L;
 }
 
-// Backward workspace regions.
+// Backward workspace regions (full: all three branches, nsa_backward).
 struct BwdLayout {
-  size_t bimg, delta, dos, revmap, lists, counts, items, slot_base, slot_cnt, nitems, part, total;
+  size_t bimg, delta, dos, revmap, lists, counts, items, slot_base, slot_cnt, nitems, part;
+  size_t pimg, dos_w, dos_c, delta_w, delta_c, dq32, slot_base_c, slot_cnt_c, total;
 };
-BwdLayout bwd_layout(const Shape& s, size_t es) {
+BwdLayout bwd_layout(const Shape& s, size_t es, bool full) {
   BwdLayout L;
   size_t o = 0;
   const size_t nblk = s.T / 64, NJ = (size_t)s.B * s.Hkv * nblk;
+  const size_t NJc = (size_t)s.B * s.Hkv * ((s.nc + 63) / 64);
+  const size_t rows = (size_t)s.B * s.Hq * s.T, elems = rows * s.D;
   L.bimg = o;      o += up(NJ * 3 * 64 * s.D * es, kAlign);
-  L.delta = o;     o += up((size_t)s.B * s.Hq * s.T * 4, kAlign);
-  L.dos = o;       o += up((size_t)s.B * s.T * s.Hq * s.D * es, kAlign);
+  L.delta = o;     o += up(rows * 4, kAlign);
+  L.dos = o;       o += up(elems * es, kAlign);
   L.revmap = o;    o += up(NJ * nblk * 8, kAlign);
   L.lists = o;     o += up(NJ * s.T * 2, kAlign);
   L.counts = o;    o += up(NJ * 4, kAlign);
-  L.items = o;     o += up(nsa::bwd_items_bytes(s), kAlign);
+  L.items = o;     o += up(nsa::bwd_items_bytes(s, full), kAlign);
   L.slot_base = o; o += up(NJ * 4, kAlign);
   L.slot_cnt = o;  o += up(NJ * 4, kAlign);
   L.nitems = o;    o += up(4, kAlign);
-  L.part = o;      o += up(nsa::bwd_part_floats(s) * 4, kAlign);
+  L.part = o;      o += up(nsa::bwd_part_floats(s, full) * 4, kAlign);
+  L.pimg = L.dos_w = L.dos_c = L.delta_w = L.delta_c = L.dq32 = L.slot_base_c = L.slot_cnt_c = 0;
+  if (full) {
+    L.pimg = o;        o += up(NJc * 3 * 64 * s.D * es, kAlign);
+    L.dos_w = o;       o += up(elems * es, kAlign);
+    L.dos_c = o;       o += up(elems * es, kAlign);
+    L.delta_w = o;     o += up(rows * 4, kAlign);
+    L.delta_c = o;     o += up(rows * 4, kAlign);
+    L.dq32 = o;        o += up(elems * 4, kAlign);
+    L.slot_base_c = o; o += up(NJc * 4, kAlign);
+    L.slot_cnt_c = o;  o += up(NJc * 4, kAlign);
+  }
   L.total = o;
   return L;
+}
+
+nsa::BwdPlanWs plan_ws(char* ws, const BwdLayout& L) {
+  nsa::BwdPlanWs pw;
+  pw.items = ws + L.items;
+  pw.lists = (uint16_t*)(ws + L.lists);
+  pw.counts = (int*)(ws + L.counts);
+  pw.slot_base = (int*)(ws + L.slot_base);
+  pw.slot_cnt = (int*)(ws + L.slot_cnt);
+  pw.slot_base_c = L.slot_base_c ? (int*)(ws + L.slot_base_c) : nullptr;
+  pw.slot_cnt_c = L.slot_cnt_c ? (int*)(ws + L.slot_cnt_c) : nullptr;
+  pw.nitems = (int*)(ws + L.nitems);
+  pw.part = (float*)(ws + L.part);
+  return pw;
 }
 
 inline size_t esize(const nsa_params_t* p) { return p->dtype == NSA_BF16 ? 2 : 4; }
@@ -123,7 +151,8 @@ nsa_status_t nsa_check_params(const nsa_params_t* p) { return check(p); }
 size_t nsa_workspace_size(const nsa_params_t* p, int for_backward) {
   if (check(p) != NSA_OK) return 0;
   const Shape s = make_shape(p);
-  return for_backward ? bwd_layout(s, esize(p)).total : fwd_layout(s, esize(p)).total;
+  if (for_backward == 2) return bwd_layout(s, esize(p), true).total;
+  return for_backward ? bwd_layout(s, esize(p), false).total : fwd_layout(s, esize(p)).total;
 }
 
 nsa_status_t nsa_pool(const void* k, const void* v, const nsa_params_t* p, void* k_cmp,
@@ -158,15 +187,21 @@ nsa_status_t nsa_compress_select(const void* q, const void* k, const void* v,
   hipError_t e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, ws + L.vct, nullptr,
                                   nullptr, kcl, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, nullptr, o_cmp, nullptr,
-                             indices, true, hs);
+  e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, o_cmp, nullptr, indices, true, hs);
   return launched(e);
 }
 
-nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, const void* gates,
-                                 const nsa_params_t* p, void* out, int32_t* indices,
-                                 float* lse_sel, void* o_sel, void* workspace, size_t ws_bytes,
-                                 void* stream, void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// The forward with every optional output: indices (output, or input with
+// NSA_INDICES_IN), the selection / window / compression log-sum-exps and
+// ungated branch outputs (each nullable; o_cmp_out replaces the workspace copy).
+nsa_status_t forward_impl(const void* q, const void* k, const void* v, const void* gates,
+                          const nsa_params_t* p, void* out, int32_t* indices, float* lse_sel,
+                          void* o_sel, float* lse_win, void* o_win, float* lse_cmp, void* o_cmp_out,
+                          void* workspace, size_t ws_bytes, void* stream, void* const* events) {
   nsa_status_t st = check(p);
   if (st != NSA_OK) return st;
   if (!q || !k || !v || !gates || !out) return NSA_ERR_NULL;
@@ -179,7 +214,9 @@ nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, co
   if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(out) ||
       (indices && !aligned16(indices)) || (lse_sel && !aligned16(lse_sel)) ||
-      (o_sel && !aligned16(o_sel)) || ((uintptr_t)workspace % kAlign) != 0)
+      (o_sel && !aligned16(o_sel)) || (lse_win && !aligned16(lse_win)) ||
+      (o_win && !aligned16(o_win)) || (lse_cmp && !aligned16(lse_cmp)) ||
+      (o_cmp_out && !aligned16(o_cmp_out)) || ((uintptr_t)workspace % kAlign) != 0)
     return NSA_ERR_ALIGN;
 
   char* ws = (char*)workspace;
@@ -189,8 +226,9 @@ nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, co
   const bool sel_out = !(p->flags & NSA_SKIP_SEL);
   const bool need_sel = sel_out || lse_sel || o_sel;
   const bool need_topk = !idx_in && (need_sel || indices);
-  const bool need_k2 = cmp_out || need_topk;
+  const bool need_k2 = cmp_out || need_topk || lse_cmp || o_cmp_out;
   int32_t* idx = indices ? indices : (int32_t*)(ws + L.indices);
+  void* o_cmp = o_cmp_out ? o_cmp_out : ws + L.o_cmp;
 
   void* kcl = bf ? ws + L.kcl : nullptr;
   auto mark = [&](int i) {
@@ -202,16 +240,41 @@ nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, co
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   mark(1);
   if (need_k2) {
-    e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct, nullptr,
-                               cmp_out ? ws + L.o_cmp : nullptr, nullptr, idx, need_topk, hs);
+    e = nsa::launch_cmp_select(bf, s, q, ws + L.kc, kcl, ws + L.vct,
+                               (cmp_out || o_cmp_out) ? o_cmp : nullptr, lse_cmp, idx, need_topk, hs);
     if (e != hipSuccess) return NSA_ERR_LAUNCH;
   }
   mark(2);
-  e = nsa::launch_sel_win(bf, s, q, k, ws + L.kvimg, gates, ws + L.o_cmp,
-                          (const float*)(ws + L.knorm), idx, out, lse_sel, o_sel, hs);
+  e = nsa::launch_sel_win(bf, s, q, k, ws + L.kvimg, gates, o_cmp, (const float*)(ws + L.knorm), idx,
+                          out, lse_sel, o_sel, lse_win, o_win, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   mark(3);
   return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status_t nsa_forward_profile(const void* q, const void* k, const void* v, const void* gates,
+                                 const nsa_params_t* p, void* out, int32_t* indices,
+                                 float* lse_sel, void* o_sel, void* workspace, size_t ws_bytes,
+                                 void* stream, void* const* events) {
+  return forward_impl(q, k, v, gates, p, out, indices, lse_sel, o_sel, nullptr, nullptr, nullptr,
+                      nullptr, workspace, ws_bytes, stream, events);
+}
+
+nsa_status_t nsa_forward_train(const void* q, const void* k, const void* v, const void* gates,
+                               const nsa_params_t* p, void* out, const nsa_saved_t* sv,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!sv || !sv->indices || !sv->lse_sel || !sv->lse_win || !sv->lse_cmp || !sv->o_sel ||
+      !sv->o_win || !sv->o_cmp)
+    return NSA_ERR_NULL;
+  if (p->flags & ~(uint32_t)NSA_INDICES_IN) return NSA_ERR_UNSUPPORTED;
+  return forward_impl(q, k, v, gates, p, out, sv->indices, sv->lse_sel, sv->o_sel, sv->lse_win,
+                      sv->o_win, sv->lse_cmp, sv->o_cmp, workspace, ws_bytes, stream, nullptr);
 }
 
 nsa_status_t nsa_forward(const void* q, const void* k, const void* v, const void* gates,
@@ -232,7 +295,7 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   if (!workspace) return NSA_ERR_WORKSPACE;
   const Shape s = make_shape(p);
   const size_t es = esize(p);
-  const BwdLayout L = bwd_layout(s, es);
+  const BwdLayout L = bwd_layout(s, es, false);
   if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(indices) ||
       !aligned16(lse_sel) || !aligned16(o_sel) || !aligned16(dout) || !aligned16(dq) ||
@@ -242,23 +305,75 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
   const bool bf = p->dtype == NSA_BF16;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = nsa::launch_bwd_prep(bf, s, k, v, gates, o_sel, dout, ws + L.bimg,
-                                      (float*)(ws + L.delta), ws + L.dos, hs);
+                                      (float*)(ws + L.delta), ws + L.dos, nullptr, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_revmap(s, indices, (uint64_t*)(ws + L.revmap), hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_dq(bf, s, q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta),
-                         ws + L.dos, dq, hs);
+  nsa::DqArgs da{q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
+                 nullptr, nullptr, dq};
+  e = nsa::launch_bwd_dq(bf, s, 0, da, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  nsa::BwdPlanWs pw;
-  pw.items = ws + L.items;
-  pw.lists = (uint16_t*)(ws + L.lists);
-  pw.counts = (int*)(ws + L.counts);
-  pw.slot_base = (int*)(ws + L.slot_base);
-  pw.slot_cnt = (int*)(ws + L.slot_cnt);
-  pw.nitems = (int*)(ws + L.nitems);
-  pw.part = (float*)(ws + L.part);
-  e = nsa::launch_bwd_dkdv(bf, s, q, ws + L.bimg, lse_sel, (const float*)(ws + L.delta), ws + L.dos,
-                           (const uint64_t*)(ws + L.revmap), dk, dv, pw, hs);
+  nsa::KvBranches br{false, q, ws + L.bimg, nullptr,
+                     {lse_sel, nullptr, nullptr},
+                     {(const float*)(ws + L.delta), nullptr, nullptr},
+                     {ws + L.dos, nullptr, nullptr}};
+  e = nsa::launch_bwd_dkdv(bf, s, br, (const uint64_t*)(ws + L.revmap), dk, dv, plan_ws(ws, L), hs);
+  return launched(e);
+}
+
+nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const void* gates,
+                          const nsa_saved_t* sv, const void* dout, const nsa_params_t* p, void* dq,
+                          void* dk, void* dv, void* dgates, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !gates || !sv || !dout || !dq || !dk || !dv || !dgates) return NSA_ERR_NULL;
+  if (!sv->indices || !sv->lse_sel || !sv->lse_win || !sv->lse_cmp || !sv->o_sel || !sv->o_win ||
+      !sv->o_cmp)
+    return NSA_ERR_NULL;
+  if (p->flags & ~(uint32_t)NSA_INDICES_IN) return NSA_ERR_UNSUPPORTED;
+  if (!workspace) return NSA_ERR_WORKSPACE;
+  const Shape s = make_shape(p);
+  const size_t es = esize(p);
+  const BwdLayout L = bwd_layout(s, es, true);
+  if (ws_bytes < L.total) return NSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(dout) ||
+      !aligned16(sv->indices) || !aligned16(sv->lse_sel) || !aligned16(sv->lse_win) ||
+      !aligned16(sv->lse_cmp) || !aligned16(sv->o_sel) || !aligned16(sv->o_win) ||
+      !aligned16(sv->o_cmp) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(dgates) || ((uintptr_t)workspace % kAlign) != 0)
+    return NSA_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  const bool bf = p->dtype == NSA_BF16;
+  hipStream_t hs = (hipStream_t)stream;
+  nsa::PrepFullArgs fx{sv->o_win, sv->o_cmp, ws + L.dos_w, ws + L.dos_c, (float*)(ws + L.delta_w),
+                       (float*)(ws + L.delta_c), dgates};
+  hipError_t e = nsa::launch_bwd_prep(bf, s, k, v, gates, sv->o_sel, dout, ws + L.bimg,
+                                      (float*)(ws + L.delta), ws + L.dos, &fx, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_pool_image(bf, s, k, v, ws + L.pimg, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_revmap(s, sv->indices, (uint64_t*)(ws + L.revmap), hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  // dq: selection, window and compression passes accumulate in fp32; the last
+  // one rounds once
+  float* dq32 = (float*)(ws + L.dq32);
+  nsa::DqArgs d0{q, ws + L.bimg, sv->indices, sv->lse_sel, (const float*)(ws + L.delta), ws + L.dos,
+                 nullptr, dq32, nullptr};
+  nsa::DqArgs d1{q, ws + L.bimg, nullptr, sv->lse_win, (const float*)(ws + L.delta_w), ws + L.dos_w,
+                 dq32, dq32, nullptr};
+  nsa::DqArgs d2{q, ws + L.pimg, nullptr, sv->lse_cmp, (const float*)(ws + L.delta_c), ws + L.dos_c,
+                 dq32, nullptr, dq};
+  e = nsa::launch_bwd_dq(bf, s, 0, d0, hs);
+  if (e == hipSuccess) e = nsa::launch_bwd_dq(bf, s, 1, d1, hs);
+  if (e == hipSuccess) e = nsa::launch_bwd_dq(bf, s, 2, d2, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  nsa::KvBranches br{true, q, ws + L.bimg, ws + L.pimg,
+                     {sv->lse_sel, sv->lse_win, sv->lse_cmp},
+                     {(const float*)(ws + L.delta), (const float*)(ws + L.delta_w),
+                      (const float*)(ws + L.delta_c)},
+                     {ws + L.dos, ws + L.dos_w, ws + L.dos_c}};
+  e = nsa::launch_bwd_dkdv(bf, s, br, (const uint64_t*)(ws + L.revmap), dk, dv, plan_ws(ws, L), hs);
   return launched(e);
 }
 

@@ -32,34 +32,12 @@ template <> struct V16b<bf16> { typedef bf16x8 type; };
 template <> struct V16b<float> { typedef f32x4 type; };
 
 // ============================================================ B0: preparation
-// grid (nblk, Hkv, B), 256 threads: block j of positions / keys, KV group g.
-// Writes the block's backward image (K, V, K^T fragments, BwdImage) and, for
-// the G heads of the group at these positions, dOs = g_sel dO and Delta.
+// Backward image of one 64-key block from its K and V rows staged in LDS
+// (kt, vt: [64][D + 8]): K and V fragments in K3's A-operand order, then K^T.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restrict__ k,
-                                                       const T* __restrict__ v,
-                                                       const T* __restrict__ gates,
-                                                       const T* __restrict__ o_sel,
-                                                       const T* __restrict__ dout,
-                                                       unsigned char* __restrict__ bimg,
-                                                       float* __restrict__ delta,
-                                                       T* __restrict__ dos) {
+__device__ void write_bwd_image(const T (*kt)[D + 8], const T (*vt)[D + 8], unsigned char* img) {
   typedef BwdImage<T, D> I;
   constexpr int EPV = 16 / sizeof(T);
-  typedef typename V16b<T>::type Vec;
-  __shared__ __align__(16) T kt[kBlock][D + 8];
-  __shared__ __align__(16) T vt[kBlock][D + 8];
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = s.G;
-  const size_t k_row = (size_t)s.Hkv * D;
-  for (int i = threadIdx.x; i < kBlock * (D / EPV); i += 256) {
-    const int r = i / (D / EPV), c8 = i % (D / EPV);
-    const size_t src = ((size_t)b * s.T + j * kBlock + r) * k_row + (size_t)g * D + c8 * EPV;
-    *reinterpret_cast<Vec*>(&kt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(k + src);
-    *reinterpret_cast<Vec*>(&vt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(v + src);
-  }
-  __syncthreads();
-  unsigned char* img = bimg + (((size_t)b * s.Hkv + g) * (s.T / kBlock) + j) * (size_t)I::BYTES;
   for (int w = threadIdx.x; w < I::PIECES * 64; w += 256) {
     const int pc = w / 64, l = w % 64;
     const int f = pc / I::NV, vv = pc % I::NV;
@@ -80,31 +58,146 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
     }
     *reinterpret_cast<f32x4*>(img + (size_t)pc * 1024 + 16 * l) = *reinterpret_cast<const f32x4*>(piece);
   }
+}
+
+// grid (nblk, Hkv, B), 256 threads: block j of positions / keys, KV group g.
+// Writes the block's backward image and, for the G heads of the group at
+// these positions, dOs = g_sel dO and Delta = dOs . o_sel.  With `full`
+// (dgates != nullptr) also the window and compression branches' dOs and
+// Delta and the gate gradients dgates = (dO . o_cmp, dO . o_sel, dO . o_win).
+struct PrepFull {
+  const void* o_win;
+  const void* o_cmp;
+  void* dos_w;
+  void* dos_c;
+  float* delta_w;
+  float* delta_c;
+  void* dgates;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restrict__ k,
+                                                       const T* __restrict__ v,
+                                                       const T* __restrict__ gates,
+                                                       const T* __restrict__ o_sel,
+                                                       const T* __restrict__ dout,
+                                                       unsigned char* __restrict__ bimg,
+                                                       float* __restrict__ delta,
+                                                       T* __restrict__ dos, PrepFull fx) {
+  typedef BwdImage<T, D> I;
+  constexpr int EPV = 16 / sizeof(T);
+  typedef typename V16b<T>::type Vec;
+  __shared__ __align__(16) T kt[kBlock][D + 8];
+  __shared__ __align__(16) T vt[kBlock][D + 8];
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = s.G;
+  const size_t k_row = (size_t)s.Hkv * D;
+  for (int i = threadIdx.x; i < kBlock * (D / EPV); i += 256) {
+    const int r = i / (D / EPV), c8 = i % (D / EPV);
+    const size_t src = ((size_t)b * s.T + j * kBlock + r) * k_row + (size_t)g * D + c8 * EPV;
+    *reinterpret_cast<Vec*>(&kt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(k + src);
+    *reinterpret_cast<Vec*>(&vt[r][c8 * EPV]) = *reinterpret_cast<const Vec*>(v + src);
+  }
+  __syncthreads();
+  write_bwd_image<T, D>(kt, vt, bimg + (((size_t)b * s.Hkv + g) * (s.T / kBlock) + j) * (size_t)I::BYTES);
   // dOs and Delta for the G heads of the group: D / EPV consecutive lanes per
   // (position, head) row, 16-byte accesses
   constexpr int TPR = D / EPV;
   static_assert((kBlock * TPR) % 256 == 0, "whole passes");
-#pragma unroll 4
+  const bool full = fx.dgates != nullptr;
   for (int i = threadIdx.x; i < kBlock * G * TPR; i += 256) {
     const int row = i / TPR, c = i % TPR;
     const int t = j * kBlock + row / G, h = g * G + row % G;
     const size_t base = (((size_t)b * s.T + t) * s.Hq + h) * D + c * EPV;
-    const float gs = (float)gates[(((size_t)b * s.T + t) * s.Hq + h) * 3 + 1];
+    const T* grow = gates + (((size_t)b * s.T + t) * s.Hq + h) * 3;
+    const float gs = (float)grow[1];
     const Vec dv = *reinterpret_cast<const Vec*>(dout + base);
     const Vec ov = *reinterpret_cast<const Vec*>(o_sel + base);
     Vec outv;
-    float acc = 0.f;
+    float acc = 0.f, dg[3] = {0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       const float x = gs * (float)dv[e];
       outv[e] = (T)x;
       acc += x * (float)ov[e];
+      dg[1] += (float)dv[e] * (float)ov[e];
     }
     *reinterpret_cast<Vec*>(dos + base) = outv;
+    float accw = 0.f, accc = 0.f;
+    if (full) {
+      const float gc = (float)grow[0], gw = (float)grow[2];
+      const Vec wv = *reinterpret_cast<const Vec*>((const T*)fx.o_win + base);
+      const Vec cv = *reinterpret_cast<const Vec*>((const T*)fx.o_cmp + base);
+      Vec ow_, oc_;
 #pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (c == 0) delta[((size_t)b * s.Hq + h) * s.T + t] = acc;
+      for (int e = 0; e < EPV; ++e) {
+        const float d0 = (float)dv[e];
+        const float xw = gw * d0, xc = gc * d0;
+        ow_[e] = (T)xw;
+        oc_[e] = (T)xc;
+        accw += xw * (float)wv[e];
+        accc += xc * (float)cv[e];
+        dg[0] += d0 * (float)cv[e];
+        dg[2] += d0 * (float)wv[e];
+      }
+      *reinterpret_cast<Vec*>((T*)fx.dos_w + base) = ow_;
+      *reinterpret_cast<Vec*>((T*)fx.dos_c + base) = oc_;
+    }
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) {
+      acc += __shfl_xor(acc, off);
+      if (full) {
+        accw += __shfl_xor(accw, off);
+        accc += __shfl_xor(accc, off);
+#pragma unroll
+        for (int z = 0; z < 3; ++z) dg[z] += __shfl_xor(dg[z], off);
+      }
+    }
+    if (c == 0) {
+      const size_t r = ((size_t)b * s.Hq + h) * s.T + t;
+      delta[r] = acc;
+      if (full) {
+        fx.delta_w[r] = accw;
+        fx.delta_c[r] = accc;
+        T* dgo = (T*)fx.dgates + (((size_t)b * s.T + t) * s.Hq + h) * 3;
+#pragma unroll
+        for (int z = 0; z < 3; ++z) dgo[z] = (T)dg[z];
+      }
+    }
   }
+}
+
+// Backward image of the pooled keys: grid (ceil(nc / 64), Hkv, B), 256
+// threads; pooled "block" J holds the pooled keys / values 64 J .. 64 J + 63
+// (the mean of the 64 tokens of each block, rounded once to T; zero past the
+// last complete block) in the BwdImage layout, so the backward kernels treat
+// the compressed branch's keys like a key block.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pool_image_kernel(Shape s, const T* __restrict__ k,
+                                                             const T* __restrict__ v,
+                                                             unsigned char* __restrict__ pimg) {
+  typedef BwdImage<T, D> I;
+  __shared__ __align__(16) T kt[kBlock][D + 8];
+  __shared__ __align__(16) T vt[kBlock][D + 8];
+  const int J = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const size_t k_row = (size_t)s.Hkv * D;
+  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
+    const int r = i / D, d = i % D;
+    const int jj = J * kBlock + r;  // pooled key = block jj of tokens
+    float sk = 0.f, sv = 0.f;
+    if (jj < s.nc) {
+      const size_t src = ((size_t)b * s.T + (size_t)jj * kBlock) * k_row + (size_t)g * D + d;
+      for (int tt = 0; tt < kBlock; ++tt) {
+        sk += (float)k[src + (size_t)tt * k_row];
+        sv += (float)v[src + (size_t)tt * k_row];
+      }
+    }
+    kt[r][d] = (T)(sk * (1.f / kBlock));
+    vt[r][d] = (T)(sv * (1.f / kBlock));
+  }
+  __syncthreads();
+  const int NJc = (s.nc + kBlock - 1) / kBlock;
+  write_bwd_image<T, D>(kt, vt, pimg + (((size_t)b * s.Hkv + g) * NJc + J) * (size_t)I::BYTES);
 }
 
 // ============================================================ B1: reverse map
@@ -132,22 +225,43 @@ __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* 
 // ============================================================ launchers
 hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* v,
                            const void* gates, const void* o_sel, const void* dout, void* bimg,
-                           float* delta, void* dos, hipStream_t st) {
+                           float* delta, void* dos, const PrepFullArgs* full, hipStream_t st) {
   dim3 grid(s.T / kBlock, s.Hkv, s.B);
   unsigned char* im = (unsigned char*)bimg;
+  PrepFull fx{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (full) fx = PrepFull{full->o_win, full->o_cmp, full->dos_w, full->dos_c, full->delta_w,
+                          full->delta_c, full->dgates};
   if (is_bf16) {
     if (s.D == 64)
       hipLaunchKernelGGL((bwd_prep_kernel<bf16, 64>), grid, dim3(256), 0, st, s, (const bf16*)k,
                          (const bf16*)v, (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout,
-                         im, delta, (bf16*)dos);
+                         im, delta, (bf16*)dos, fx);
     else
       hipLaunchKernelGGL((bwd_prep_kernel<bf16, 128>), grid, dim3(256), 0, st, s, (const bf16*)k,
                          (const bf16*)v, (const bf16*)gates, (const bf16*)o_sel, (const bf16*)dout,
-                         im, delta, (bf16*)dos);
+                         im, delta, (bf16*)dos, fx);
   } else {
     hipLaunchKernelGGL((bwd_prep_kernel<float, 64>), grid, dim3(256), 0, st, s, (const float*)k,
                        (const float*)v, (const float*)gates, (const float*)o_sel,
-                       (const float*)dout, im, delta, (float*)dos);
+                       (const float*)dout, im, delta, (float*)dos, fx);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* k, const void* v,
+                                 void* pimg, hipStream_t st) {
+  dim3 grid((s.nc + kBlock - 1) / kBlock, s.Hkv, s.B);
+  unsigned char* im = (unsigned char*)pimg;
+  if (is_bf16) {
+    if (s.D == 64)
+      hipLaunchKernelGGL((bwd_pool_image_kernel<bf16, 64>), grid, dim3(256), 0, st, s,
+                         (const bf16*)k, (const bf16*)v, im);
+    else
+      hipLaunchKernelGGL((bwd_pool_image_kernel<bf16, 128>), grid, dim3(256), 0, st, s,
+                         (const bf16*)k, (const bf16*)v, im);
+  } else {
+    hipLaunchKernelGGL((bwd_pool_image_kernel<float, 64>), grid, dim3(256), 0, st, s,
+                       (const float*)k, (const float*)v, im);
   }
   return hipGetLastError();
 }

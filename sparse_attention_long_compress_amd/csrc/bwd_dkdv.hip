@@ -40,7 +40,44 @@ namespace nsa {
 // LDS list of the dk/dv kernel); blocks with several items get one partial
 // slot per item.
 struct Item {
-  int bg, j, lo, hi, slot;  // (batch, group) index, block, positions [lo, hi) of its list, slot or -1
+  int bg, j, lo, hi, slot;  // (batch, group) index, block, rows [lo, hi), partial slot or -1
+  int mode;                 // KV_SEL: [lo, hi) indexes the block's position list;
+                            // KV_WIN, KV_CMP: positions lo .. hi - 1 themselves
+};
+
+// Branch of a dk/dv item: selection rows (position lists), window rows
+// (positions 64 j .. 64 j + 62 + W) or compression rows (positions from
+// 64 (64 j + 1) - 1 on) against the pooled-key block j (pooled keys 64 j ..).
+enum { KV_SEL = 0, KV_WIN = 1, KV_CMP = 2 };
+
+// key (a token index, or a pooled-key index for KV_CMP) visible to row position t
+__device__ __forceinline__ bool kv_allowed(int mode, int key, int t, int W) {
+  if (mode == KV_SEL) return key <= t;
+  if (mode == KV_WIN) return key <= t && key > t - W;
+  return key < (t + 1) / kBlock;
+}
+// whether a chunk of rows with positions first .. last (ascending) needs the
+// element mask against block j
+__device__ __forceinline__ bool kv_chunk_masked(int mode, int j, int first, int last, int W) {
+  if (mode == KV_SEL) return first < j * kBlock + kBlock - 1;
+  if (mode == KV_WIN) return first < j * kBlock + kBlock - 1 || last >= j * kBlock + W;
+  return (first + 1) / kBlock < j * kBlock + kBlock;
+}
+
+// Arguments of the dk/dv kernels: per-branch log-sum-exp, Delta and dOs
+// (indexed by the item's mode), the block images and the pooled-key images.
+struct KvArgs {
+  const void* q;
+  const unsigned char* img;
+  const unsigned char* pimg;
+  const uint16_t* lists;
+  const float* lse[3];
+  const float* delta[3];
+  const void* dos[3];
+  const int* nitems;
+  void* dk;
+  void* dv;
+  float* part;
 };
 
 constexpr int kItemRows = 2048;
@@ -53,12 +90,28 @@ __host__ __device__ inline int items_of(int npos, int G) {
   return n > 1 ? n : 1;
 }
 
-// Upper bound on the item count (grid size; workspace): a block has at most
-// 1 + rows / kItemRows items, and every position selects at most top_k blocks.
-int bwd_item_bound(const Shape& s) {
+// rows of the window and compression items of block j (positions)
+__host__ __device__ inline int win_positions(int j, int T, int W) {
+  const int hi = j * kBlock + kBlock - 1 + W < T ? j * kBlock + kBlock - 1 + W : T;
+  return hi - j * kBlock;
+}
+__host__ __device__ inline int cmp_first_position(int J) { return kBlock * (kBlock * J + 1) - 1; }
+
+// Upper bound on the item count (grid size; workspace): a selection block has
+// at most 1 + rows / kItemRows items and every position selects at most top_k
+// blocks; window and compression items are counted exactly.
+int bwd_item_bound(const Shape& s, bool full) {
   const long nblk = s.T / kBlock;
   const long rows = (long)s.T * s.topk * s.G;
-  return (int)((long)s.B * s.Hkv * (nblk + (rows + kItemRows - 1) / kItemRows));
+  long n = nblk + (rows + kItemRows - 1) / kItemRows;
+  if (full) {
+    for (int j = 0; j < nblk; ++j) n += items_of(win_positions(j, s.T, s.W), s.G);
+    for (int J = 0; J * kBlock < s.nc; ++J) {
+      const int pc = s.T - cmp_first_position(J);
+      if (pc > 0) n += items_of(pc, s.G);
+    }
+  }
+  return (int)((long)s.B * s.Hkv * n);
 }
 
 // B1b: grid (nblk, Hkv, B), 256 threads.  Ascending positions that selected
@@ -106,20 +159,32 @@ __global__ __launch_bounds__(256) void bwd_lists_kernel(Shape s, const uint64_t*
 }
 
 // B1c: one workgroup.  Items of every (batch, group, block) in natural order
-// (block-major), slot_base / slot_cnt per block and the item count.
-__global__ __launch_bounds__(1024) void bwd_items_kernel(int NJ, int nblk, int G, const int* __restrict__ counts,
+// (block-major): the block's selection items, then (full) its window items
+// and, for j a multiple of 64, the compression items of pooled-key block j / 64.
+// slot_base / slot_cnt per block (selection-only: -1 / 1 for a single item,
+// written directly); slot_base_c / slot_cnt_c per pooled-key block (full).
+__global__ __launch_bounds__(1024) void bwd_items_kernel(int NJ, int nblk, int G, int T, int W, int full,
+                                                        const int* __restrict__ counts,
                                                         Item* __restrict__ items, int* __restrict__ slot_base,
-                                                        int* __restrict__ slot_cnt, int* __restrict__ nitems) {
+                                                        int* __restrict__ slot_cnt, int* __restrict__ slot_base_c,
+                                                        int* __restrict__ slot_cnt_c, int* __restrict__ nitems) {
   __shared__ int wtot[2][16];
   __shared__ int carry[2];
   const int x = threadIdx.x, w = x / 64, l = x % 64;
+  const int NJc = (nblk + kBlock - 1) / kBlock;
   if (x == 0) carry[0] = carry[1] = 0;
   __syncthreads();
   for (int e0 = 0; e0 < NJ; e0 += 1024) {
     const int e = e0 + x;
+    const int j = e % nblk;
     const int P = e < NJ ? counts[e] : 0;
-    const int n = e < NJ ? items_of(P, G) : 0;
-    const int sl = n > 1 ? n : 0;
+    const int ns = e < NJ ? items_of(P, G) : 0;
+    const int pw = full ? win_positions(j, T, W) : 0;
+    const int nw = e < NJ && full ? items_of(pw, G) : 0;
+    const int pc = full && j % kBlock == 0 ? T - cmp_first_position(j / kBlock) : 0;
+    const int nc = e < NJ && pc > 0 ? items_of(pc, G) : 0;
+    const int n = ns + nw + nc;
+    const int sl = full ? n : (ns > 1 ? ns : 0);
     int in = n, is = sl;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -132,16 +197,37 @@ __global__ __launch_bounds__(1024) void bwd_items_kernel(int NJ, int nblk, int G
     for (int k = 0; k < w; ++k) { pi += wtot[0][k]; ps += wtot[1][k]; }
     const int io = pi + in - n, so = ps + is - sl;
     if (e < NJ) {
-      slot_base[e] = n > 1 ? so : -1;
-      slot_cnt[e] = n;
-      for (int i = 0; i < n; ++i) {
+      const int bg = e / nblk;
+      slot_base[e] = sl > 0 ? so : -1;
+      slot_cnt[e] = ns + nw;
+      if (full && j % kBlock == 0) {
+        slot_base_c[bg * NJc + j / kBlock] = so + ns + nw;
+        slot_cnt_c[bg * NJc + j / kBlock] = nc;
+      }
+      int k = io;
+      for (int i = 0; i < ns; ++i, ++k) {
         Item it;
-        it.bg = e / nblk;
-        it.j = e % nblk;
-        it.lo = P * i / n;  // P <= 65536, n <= P: no overflow
-        it.hi = P * (i + 1) / n;
-        it.slot = n > 1 ? so + i : -1;
-        items[io + i] = it;
+        it.bg = bg; it.j = j; it.mode = KV_SEL;
+        it.lo = P * i / ns;  // P <= 65536, n <= P: no overflow
+        it.hi = P * (i + 1) / ns;
+        it.slot = sl > 0 ? so + i : -1;
+        items[k] = it;
+      }
+      for (int i = 0; i < nw; ++i, ++k) {
+        Item it;
+        it.bg = bg; it.j = j; it.mode = KV_WIN;
+        it.lo = j * kBlock + pw * i / nw;
+        it.hi = j * kBlock + pw * (i + 1) / nw;
+        it.slot = so + ns + i;
+        items[k] = it;
+      }
+      for (int i = 0; i < nc; ++i, ++k) {
+        Item it;
+        it.bg = bg; it.j = j / kBlock; it.mode = KV_CMP;
+        it.lo = cmp_first_position(j / kBlock) + pc * i / nc;
+        it.hi = cmp_first_position(j / kBlock) + pc * (i + 1) / nc;
+        it.slot = so + ns + nw + i;
+        items[k] = it;
       }
     }
     __syncthreads();
@@ -275,10 +361,7 @@ __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
-    Shape s, const Item* __restrict__ items, const T* __restrict__ q,
-    const unsigned char* __restrict__ bimg, const float* __restrict__ lse,
-    const float* __restrict__ delta, const T* __restrict__ dos, const uint16_t* __restrict__ lists,
-    const int* __restrict__ nitems, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ part) {
+    Shape s, const Item* __restrict__ items, KvArgs args) {
   typedef KvCfg<T, D, G> C;
   constexpr int NW = C::NW, NT = C::NT, CP = C::CP, TB = C::TB, NLD = C::NLD, RPI = C::RPI;
   constexpr int SLOTS = C::SLOTS, LQ = C::LQ, STAGE = C::STAGE, NR = C::NR;
@@ -294,8 +377,17 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
   uint16_t* plist = reinterpret_cast<uint16_t*>(ring + C::RING);  // [MAXPOS]
 
   // items in block-major order (an XCD-interleaved order measured slower)
-  if ((int)blockIdx.x >= *nitems) return;
+  if ((int)blockIdx.x >= *args.nitems) return;
   const Item it = items[blockIdx.x];
+  const int mode = it.mode;
+  const T* __restrict__ q = (const T*)args.q;
+  const float* __restrict__ lse = args.lse[mode];
+  const float* __restrict__ delta = args.delta[mode];
+  const T* __restrict__ dos = (const T*)args.dos[mode];
+  T* __restrict__ dk = (T*)args.dk;
+  T* __restrict__ dv = (T*)args.dv;
+  float* __restrict__ part = args.part;
+  const int Wn = s.W;
   const int nblk = s.T / kBlock;
   const int g = it.bg % s.Hkv, b = it.bg / s.Hkv;
   const int j = it.j;
@@ -307,7 +399,9 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
 
   // K and V fragments of block j (first 2 NFRAG fragments of its backward image)
   {
-    const unsigned char* src = bimg + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES + 16 * l;
+    const unsigned char* src =
+        (mode == KV_CMP ? args.pimg + ((size_t)it.bg * ((s.nc + kBlock - 1) / kBlock) + j) * (size_t)BwdImage<T, D>::BYTES
+                        : args.img + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES) + 16 * l;
     for (int pc = w; pc < KVB / 1024; pc += NW)
       __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024), (void*)(kv + (size_t)pc * 1024),
                                        16, 0, 0);
@@ -315,8 +409,12 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
   // the item's slice of the block's ascending position list
   const int npos = it.hi - it.lo;
   {
-    const uint16_t* src = lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
-    for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
+    if (mode == KV_SEL) {
+      const uint16_t* src = args.lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
+      for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
+    } else {
+      for (int i = threadIdx.x; i < npos; i += NT) plist[i] = (uint16_t)(it.lo + i);
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -328,7 +426,6 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
   const int nch = (npos + CP - 1) / CP;
   const int my_n = nch > w ? (nch - w + NW - 1) / NW : 0;
   unsigned char* wring = ring + (size_t)w * NR * STAGE;
-  const int last_key_mask = j * kBlock + kBlock - 1;  // rows before this position need the causal mask
 
   auto issue_chunk = [&](int ck, int stage) {
     unsigned char* st = wring + (size_t)stage * STAGE;
@@ -390,7 +487,8 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
       for (int e = 0; e < 8; ++e)
         if (ck * CP + (8 * a + e) / G >= npos) lr[e] = INF;
     }
-    const bool masked = plist[ck * CP] < last_key_mask;
+    const bool masked = kv_chunk_masked(mode, j, __builtin_amdgcn_readfirstlane(plist[ck * CP]),
+                                        __builtin_amdgcn_readfirstlane(plist[min(ck * CP + CP, npos) - 1]), Wn);
 
     // A fragments of Q and dOs for the two row subtiles (row 8(rho/4) + 4u + rho%4)
     FragT qa[2][KS], da[2][KS];
@@ -430,7 +528,7 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
         for (int e = 0; e < 8; ++e) {
           const int qi = ck * CP + (8 * a + e) / G;
           const int t = plist[qi < npos ? qi : 0];
-          p[e] = key <= t ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
+          p[e] = kv_allowed(mode, key, t, Wn) ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
           x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
         }
       }
@@ -537,10 +635,7 @@ struct KvPairCfg {
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel(
-    Shape s, const Item* __restrict__ items, const T* __restrict__ q,
-    const unsigned char* __restrict__ bimg, const float* __restrict__ lse,
-    const float* __restrict__ delta, const T* __restrict__ dos, const uint16_t* __restrict__ lists,
-    const int* __restrict__ nitems, T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ part) {
+    Shape s, const Item* __restrict__ items, KvArgs args) {
   typedef KvPairCfg<T, D, G> C;
   constexpr int NT = C::NT, NP = C::NP, CP = C::CP, TB = C::TB, NLD = C::NLD, RPI = C::RPI;
   constexpr int SLOTS = C::SLOTS, STAGE = C::STAGE, NR = C::NR, L0 = C::L0, L1 = C::L1;
@@ -555,8 +650,17 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
   unsigned char* ring = smem + KVB;                                // [NP][NR][STAGE]
   uint16_t* plist = reinterpret_cast<uint16_t*>(ring + C::RING);  // [MAXPOS]
 
-  if ((int)blockIdx.x >= *nitems) return;
+  if ((int)blockIdx.x >= *args.nitems) return;
   const Item it = items[blockIdx.x];
+  const int mode = it.mode;
+  const T* __restrict__ q = (const T*)args.q;
+  const float* __restrict__ lse = args.lse[mode];
+  const float* __restrict__ delta = args.delta[mode];
+  const T* __restrict__ dos = (const T*)args.dos[mode];
+  T* __restrict__ dk = (T*)args.dk;
+  T* __restrict__ dv = (T*)args.dv;
+  float* __restrict__ part = args.part;
+  const int Wn = s.W;
   const int nblk = s.T / kBlock;
   const int g = it.bg % s.Hkv, b = it.bg / s.Hkv;
   const int j = it.j;
@@ -568,15 +672,21 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
   const size_t q_row = (size_t)s.Hq * D;
 
   {
-    const unsigned char* src = bimg + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES + 16 * l;
+    const unsigned char* src =
+        (mode == KV_CMP ? args.pimg + ((size_t)it.bg * ((s.nc + kBlock - 1) / kBlock) + j) * (size_t)BwdImage<T, D>::BYTES
+                        : args.img + ((size_t)it.bg * nblk + j) * (size_t)BwdImage<T, D>::BYTES) + 16 * l;
     for (int pc = w; pc < KVB / 1024; pc += C::NW)
       __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024), (void*)(kv + (size_t)pc * 1024),
                                        16, 0, 0);
   }
   const int npos = it.hi - it.lo;
   {
-    const uint16_t* src = lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
-    for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
+    if (mode == KV_SEL) {
+      const uint16_t* src = args.lists + ((size_t)it.bg * nblk + j) * (size_t)s.T + it.lo;
+      for (int i = threadIdx.x; i < npos; i += NT) plist[i] = src[i];
+    } else {
+      for (int i = threadIdx.x; i < npos; i += NT) plist[i] = (uint16_t)(it.lo + i);
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -587,7 +697,6 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
 
   const int nch = (npos + CP - 1) / CP;
   const int rounds = (nch + NP - 1) / NP;
-  const int last_key_mask = j * kBlock + kBlock - 1;
   unsigned char* pring = ring + (size_t)pr * NR * STAGE;
   auto has = [&](int r) { return r * NP + pr < nch; };
 
@@ -677,7 +786,8 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
       for (int e = 0; e < 8; ++e)
         if (ck * CP + (8 * a + e) / G >= npos) lr[e] = INF;
     }
-    const bool masked = __builtin_amdgcn_readfirstlane(plist[ck * CP]) < last_key_mask;
+    const bool masked = kv_chunk_masked(mode, j, __builtin_amdgcn_readfirstlane(plist[ck * CP]),
+                                        __builtin_amdgcn_readfirstlane(plist[min(ck * CP + CP, npos) - 1]), Wn);
 
     FragT qa[2][KS], da[2][KS];
 #pragma unroll
@@ -715,7 +825,7 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
         for (int e = 0; e < 8; ++e) {
           const int qi = ck * CP + (8 * a + e) / G;
           const int t = plist[qi < npos ? qi : 0];
-          p[e] = key <= t ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
+          p[e] = kv_allowed(mode, key, t, Wn) ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
           x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
         }
       }
@@ -784,16 +894,22 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
 
 // ------------------------------------------------------------------ B4
 // grid (B Hkv nblk): the partial sums of a block's items, added in item order,
-// rows staged in LDS for 16-byte stores.
+// rows staged in LDS for 16-byte stores.  With the compression branch
+// (slot_base_c != nullptr) the pooled key j of pooled-key block j / 64 adds
+// its gradient (the sum of that block's compression partials, row j % 64)
+// divided by 64 to every key of block j: the gradient of the mean-pool.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Shape s, const int* __restrict__ slot_base,
                                                          const int* __restrict__ slot_cnt,
+                                                         const int* __restrict__ slot_base_c,
+                                                         const int* __restrict__ slot_cnt_c,
                                                          const float* __restrict__ part,
                                                          T* __restrict__ dk, T* __restrict__ dv) {
   typedef typename BwdImage<T, D>::K KI;
   constexpr int MT = D / 16, NFR = 4 * MT;
   constexpr int PER = 2 * NFR * 64 / 256;  // fragment entries (4 floats) per thread
   __shared__ __align__(16) float ot[2][kBlock * D];
+  __shared__ float pooled[2][D];
   const int e = blockIdx.x;
   const int base = slot_base[e];
   if (base < 0) return;
@@ -801,6 +917,22 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Shape s, const int* __r
   const int nblk = s.T / kBlock;
   const int bg = e / nblk, j = e % nblk;
   const int g = bg % s.Hkv, b = bg / s.Hkv;
+  const bool full = slot_base_c != nullptr;
+  if (full) {
+    // row jj = j % 64 of the pooled-key block's partials: fragment v, lane group
+    // a, register r hold key jj (inverse of the image's key order), lane col channel
+    const int NJc = (s.nc + kBlock - 1) / kBlock;
+    const int ec = bg * NJc + j / kBlock, jj = j % kBlock;
+    const int cb = slot_base_c[ec], cn = slot_cnt_c[ec];
+    const int v = 2 * (jj / 32) + (jj % 8) / 4, a = (jj % 32) / 8, r = jj % 4;
+    for (int i = threadIdx.x; i < 2 * D; i += 256) {
+      const int tns = i / D, ch = i % D, m = ch / 16, col = ch % 16;
+      float acc = 0.f;
+      for (int z = 0; z < cn; ++z)
+        acc += part[((size_t)(cb + z) * 2 + tns) * NFR * 256 + ((size_t)(v * MT + m) * 64 + 16 * a + col) * 4 + r];
+      pooled[tns][ch] = acc * (1.f / kBlock);
+    }
+  }
   const float* pb = part + (size_t)base * 2 * NFR * 256;
   f32x4 sum[PER];
 #pragma unroll
@@ -810,14 +942,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Shape s, const int* __r
 #pragma unroll
     for (int k = 0; k < PER; ++k) sum[k] += *reinterpret_cast<const f32x4*>(pz + ((size_t)threadIdx.x + 256 * k) * 4);
   }
+  __syncthreads();  // pooled row visible
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int i = threadIdx.x + 256 * k;
     const int tns = i / (NFR * 64), fi = (i / 64) % NFR, l = i % 64;
     const int v = fi / MT, m = fi % MT, a = l >> 4, col = l & 15;
     const float sc = tns == 0 ? s.scale : 1.f;
+    const float add = full ? pooled[tns][16 * m + col] : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ot[tns][KI::krow(v, 4 * a + r) * D + 16 * m + col] = sum[k][r] * sc;
+    for (int r = 0; r < 4; ++r) ot[tns][KI::krow(v, 4 * a + r) * D + 16 * m + col] = (sum[k][r] + add) * sc;
   }
   __syncthreads();
   const size_t k_row = (size_t)s.Hkv * D;
@@ -831,97 +965,100 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Shape s, const int* __r
 
 // ------------------------------------------------------------------ launchers
 template <typename T, int D, int G>
-static hipError_t launch_kv_t(const Shape& s, const Item* items, int grid_items, const int* nitems,
-                              const void* q, const void* bimg, const float* lse, const float* delta,
-                              const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+static hipError_t launch_kv_t(const Shape& s, const Item* items, int grid_items, const KvArgs& a,
                               hipStream_t st) {
   typedef KvCfg<T, D, G> C;
   hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, G>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, G>), dim3(grid_items), dim3(C::NT), C::LDS, st, s, items,
-                     (const T*)q, (const unsigned char*)bimg, lse, delta, (const T*)dos, lists, nitems,
-                     (T*)dk, (T*)dv, part);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, G>), dim3(grid_items), dim3(C::NT), C::LDS, st, s, items, a);
   return hipGetLastError();
 }
 template <int G>
-static hipError_t launch_kv_pair(const Shape& s, const Item* items, int grid_items, const int* nitems,
-                                 const void* q, const void* bimg, const float* lse, const float* delta,
-                                 const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+static hipError_t launch_kv_pair(const Shape& s, const Item* items, int grid_items, const KvArgs& a,
                                  hipStream_t st) {
   typedef KvPairCfg<bf16, 64, G> C;
   hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_pair_kernel<bf16, 64, G>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_pair_kernel<bf16, 64, G>), dim3(grid_items), dim3(C::NT), C::LDS, st, s,
-                     items, (const bf16*)q, (const unsigned char*)bimg, lse, delta, (const bf16*)dos, lists,
-                     nitems, (bf16*)dk, (bf16*)dv, part);
+                     items, a);
   return hipGetLastError();
 }
-
 template <typename T, int D>
-static hipError_t launch_kv_g(const Shape& s, const Item* items, int grid_items, const int* nitems,
-                              const void* q, const void* bimg, const float* lse, const float* delta,
-                              const void* dos, const uint16_t* lists, void* dk, void* dv, float* part,
+static hipError_t launch_kv_g(const Shape& s, const Item* items, int grid_items, const KvArgs& a,
                               hipStream_t st) {
-#define NSA_KV(GG) launch_kv_t<T, D, GG>(s, items, grid_items, nitems, q, bimg, lse, delta, dos, lists, dk, dv, part, st)
   switch (s.G) {
-    case 1: return NSA_KV(1);
-    case 2: return NSA_KV(2);
-    case 4: return NSA_KV(4);
-    case 8: return NSA_KV(8);
-    default: return NSA_KV(16);
+    case 1: return launch_kv_t<T, D, 1>(s, items, grid_items, a, st);
+    case 2: return launch_kv_t<T, D, 2>(s, items, grid_items, a, st);
+    case 4: return launch_kv_t<T, D, 4>(s, items, grid_items, a, st);
+    case 8: return launch_kv_t<T, D, 8>(s, items, grid_items, a, st);
+    default: return launch_kv_t<T, D, 16>(s, items, grid_items, a, st);
   }
-#undef NSA_KV
 }
 
-hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* bimg,
-                           const float* lse, const float* delta, const void* dos,
-                           const uint64_t* revmap, void* dk, void* dv, const BwdPlanWs& ws,
-                           hipStream_t st) {
+hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const KvBranches& br, const uint64_t* revmap,
+                           void* dk, void* dv, const BwdPlanWs& ws, hipStream_t st) {
   const int nblk = s.T / kBlock;
   const int NJ = s.B * s.Hkv * nblk;
+  const bool full = br.full;
   Item* items = (Item*)ws.items;
   hipLaunchKernelGGL(bwd_lists_kernel, dim3(nblk, s.Hkv, s.B), dim3(256), 0, st, s, revmap, ws.lists,
                      ws.counts);
-  hipLaunchKernelGGL(bwd_items_kernel, dim3(1), dim3(1024), 0, st, NJ, nblk, s.G, ws.counts, items,
-                     ws.slot_base, ws.slot_cnt, ws.nitems);
+  hipLaunchKernelGGL(bwd_items_kernel, dim3(1), dim3(1024), 0, st, NJ, nblk, s.G, s.T, s.W, full ? 1 : 0,
+                     ws.counts, items, ws.slot_base, ws.slot_cnt, ws.slot_base_c, ws.slot_cnt_c, ws.nitems);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid_items = bwd_item_bound(s);
+  KvArgs a;
+  a.q = br.q;
+  a.img = (const unsigned char*)br.img;
+  a.pimg = (const unsigned char*)br.pimg;
+  a.lists = ws.lists;
+  for (int m = 0; m < 3; ++m) {
+    a.lse[m] = br.lse[m];
+    a.delta[m] = br.delta[m];
+    a.dos[m] = br.dos[m];
+  }
+  a.nitems = ws.nitems;
+  a.dk = dk;
+  a.dv = dv;
+  a.part = ws.part;
+  const int grid_items = bwd_item_bound(s, full);
   if (is_bf16) {
     if (s.D == 64) {
-#define NSA_KVP(GG) launch_kv_pair<GG>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st)
       switch (s.G) {
-        case 1: e = NSA_KVP(1); break;
-        case 2: e = NSA_KVP(2); break;
-        case 4: e = NSA_KVP(4); break;
-        case 8: e = NSA_KVP(8); break;
-        default: e = NSA_KVP(16); break;
+        case 1: e = launch_kv_pair<1>(s, items, grid_items, a, st); break;
+        case 2: e = launch_kv_pair<2>(s, items, grid_items, a, st); break;
+        case 4: e = launch_kv_pair<4>(s, items, grid_items, a, st); break;
+        case 8: e = launch_kv_pair<8>(s, items, grid_items, a, st); break;
+        default: e = launch_kv_pair<16>(s, items, grid_items, a, st); break;
       }
-#undef NSA_KVP
+    } else {
+      e = launch_kv_g<bf16, 128>(s, items, grid_items, a, st);
     }
-    else
-      e = launch_kv_g<bf16, 128>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
   } else {
-    e = launch_kv_g<float, 64>(s, items, grid_items, ws.nitems, q, bimg, lse, delta, dos, ws.lists, dk, dv, ws.part, st);
+    e = launch_kv_g<float, 64>(s, items, grid_items, a, st);
   }
   if (e != hipSuccess) return e;
+  const int* sbc = full ? ws.slot_base_c : nullptr;
+  const int* scc = full ? ws.slot_cnt_c : nullptr;
   if (is_bf16) {
     if (s.D == 64)
       hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 64>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
-                         ws.slot_cnt, ws.part, (bf16*)dk, (bf16*)dv);
+                         ws.slot_cnt, sbc, scc, ws.part, (bf16*)dk, (bf16*)dv);
     else
       hipLaunchKernelGGL((bwd_reduce_kernel<bf16, 128>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
-                         ws.slot_cnt, ws.part, (bf16*)dk, (bf16*)dv);
+                         ws.slot_cnt, sbc, scc, ws.part, (bf16*)dk, (bf16*)dv);
   } else {
     hipLaunchKernelGGL((bwd_reduce_kernel<float, 64>), dim3(NJ), dim3(256), 0, st, s, ws.slot_base,
-                       ws.slot_cnt, ws.part, (float*)dk, (float*)dv);
+                       ws.slot_cnt, sbc, scc, ws.part, (float*)dk, (float*)dv);
   }
   return hipGetLastError();
 }
 
-size_t bwd_items_bytes(const Shape& s) { return (size_t)bwd_item_bound(s) * sizeof(Item); }
-size_t bwd_part_floats(const Shape& s) { return (size_t)bwd_item_bound(s) * 2 * kBlock * s.D; }
+size_t bwd_items_bytes(const Shape& s, bool full) { return (size_t)bwd_item_bound(s, full) * sizeof(Item); }
+size_t bwd_part_floats(const Shape& s, bool full) {
+  return (size_t)bwd_item_bound(s, full) * 2 * kBlock * s.D;
+}
 
 }  // namespace nsa

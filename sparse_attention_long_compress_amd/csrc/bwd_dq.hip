@@ -59,11 +59,18 @@ static size_t dq_lds_bytes(int topk) {
   return (size_t)C::NBUF * C::STAGE + (size_t)C::P * topk * 2;
 }
 
-template <typename T, int D, int G>
+// Branch of a dq pass.  SEL: the selected blocks (rows that did not select a
+// block get lse2 = +inf); WIN: the blocks meeting a row's window, keys
+// t - W < s <= t; CMP: "blocks" of 64 pooled keys (the pooled-key images),
+// pooled key jj visible to t when 64 (jj + 1) - 1 <= t.
+enum { DQ_SEL = 0, DQ_WIN = 1, DQ_CMP = 2 };
+
+template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
     Shape s, const T* __restrict__ q, const unsigned char* __restrict__ bimg,
     const int32_t* __restrict__ indices, const float* __restrict__ lse,
-    const float* __restrict__ delta, const T* __restrict__ dos, T* __restrict__ dq) {
+    const float* __restrict__ delta, const T* __restrict__ dos, const float* __restrict__ acc_in,
+    float* __restrict__ acc_out, T* __restrict__ dq) {
   typedef DqCfg<T, D, G> C;
   constexpr int NT = C::NT, P = C::P, NSG = C::NSG, KS = C::KS, MT = C::MT;
   constexpr int NFRAG = C::NFRAG, FCH = C::FCH, FRAG_BYTES = C::FRAG_BYTES, STAGE = C::STAGE;
@@ -72,7 +79,7 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   typedef typename C::Img::K KI;  // fragment index helpers of the image
   const float INF = __builtin_inff();
 
-  const int nblk_all = s.T / kBlock;
+  const int nimg = MODE == DQ_CMP ? (s.nc + kBlock - 1) / kBlock : s.T / kBlock;  // images per (b, g)
   const int NTL = (s.T + P - 1) / P;
   int bg, tile;
   xcd_order(blockIdx.x, gridDim.x, s.B * s.Hkv, NTL, bg, tile);
@@ -86,17 +93,20 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   const int h = g * G + hh;
   const float c1 = s.scale * kLog2e;
   const int topk = s.topk;
+  const int W = s.W;
   const size_t q_row = (size_t)s.Hq * D;
-  const unsigned char* img_b = bimg + ((size_t)b * s.Hkv + g) * nblk_all * (size_t)STAGE;
+  const unsigned char* img_b = bimg + ((size_t)b * s.Hkv + g) * nimg * (size_t)STAGE;
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* ring = smem;                                                  // [NBUF][STAGE]
   int16_t* lists = reinterpret_cast<int16_t*>(smem + (size_t)C::NBUF * STAGE);  // [P][topk]
 
-  for (int i = threadIdx.x; i < P * topk; i += NT) {
-    const int p = i / topk, e = i % topk;
-    const int j = p < nvalid ? indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e] : -1;
-    lists[i] = (int16_t)(j < 0 ? 0x7fff : j);
+  if constexpr (MODE == DQ_SEL) {
+    for (int i = threadIdx.x; i < P * topk; i += NT) {
+      const int p = i / topk, e = i % topk;
+      const int j = p < nvalid ? indices[(((size_t)b * s.Hkv + g) * s.T + t0 + p) * topk + e] : -1;
+      lists[i] = (int16_t)(j < 0 ? 0x7fff : j);
+    }
   }
 
   // this lane's row: position p, head h
@@ -105,6 +115,8 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   const int t = t0 + p;
   const bool valid = p < nvalid;
   const int own = (t0 + pf) / kBlock;
+  const int nvf = min(max(nvalid - pf, 0), NSG);  // valid positions of the column group
+  const int tf = t0 + pf, tl = tf + max(nvf, 1) - 1;
   FragT qf[KS], df[KS];
   float lse2 = INF, dl = 0.f;
 #pragma unroll
@@ -124,11 +136,24 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   }
   __syncthreads();  // lists visible
   int ptr = 0;
-  int nxt = valid ? lists[p * topk] : 0x7fff;
-  int nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+  int nxt = 0x7fff, nsel = 0x7fff;
+  if constexpr (MODE == DQ_SEL) {
+    nxt = valid ? lists[p * topk] : 0x7fff;
+    nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+  }
+  // per column group (scalar): the window blocks and the edge block; the
+  // pooled blocks with a key visible to the group's last / first position
+  const int jw_lo = max(0, tf - W + 1) / kBlock;
+  const int jw_edge = tl >= W ? (tl - W) / kBlock : -1;
+  const int nvis_l = (tl + 1) / kBlock, nvis_f = (tf + 1) / kBlock;  // pooled keys visible
+  const int nvis = (t + 1) / kBlock;
 
-  const int c_last = (t0 + nvalid - 1) / kBlock;
-  const int nblk = c_last + 1;
+  const int t_last = t0 + nvalid - 1;
+  int j_begin = 0, j_end = 0;  // walk [j_begin, j_end)
+  if constexpr (MODE == DQ_SEL) { j_begin = 0; j_end = t_last / kBlock + 1; }
+  if constexpr (MODE == DQ_WIN) { j_begin = max(0, t0 - W + 1) / kBlock; j_end = t_last / kBlock + 1; }
+  if constexpr (MODE == DQ_CMP) { j_begin = 0; j_end = ((t_last + 1) / kBlock + kBlock - 1) / kBlock; }
+  const int nblk = max(j_end - j_begin, 0);
 
   auto issue = [&](int j, int bf) {
     unsigned char* stage = ring + (size_t)bf * STAGE;
@@ -146,24 +171,43 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   auto issue_group = [&](int gi) {
 #pragma unroll
     for (int qq = 0; qq < GB; ++qq)
-      if (gi * GB + qq < nblk) issue(gi * GB + qq, (gi & 1) * GB + qq);
+      if (gi * GB + qq < nblk) issue(j_begin + gi * GB + qq, (gi & 1) * GB + qq);
   };
-  issue_group(0);
+  if (ngrp > 0) issue_group(0);
 
   for (int gi = 0; gi < ngrp; ++gi) {
     wait_vmcnt<0>();       // this wave's loads of group gi (the only ones in flight)
     barrier_keep_loads();  // all of group gi is in LDS; group gi-1's slots are free
     if (gi + 1 < ngrp) issue_group(gi + 1);
     for (int qq = 0; qq < GB; ++qq) {
-      const int j = gi * GB + qq;
-      if (j >= nblk) break;
-      if (j != nsel) continue;  // no row of this column group selected block j
-      const bool sl = nxt == j;
-      if (sl) {
-        ++ptr;
-        nxt = ptr < topk ? lists[p * topk + ptr] : 0x7fff;
+      const int r = gi * GB + qq;
+      if (r >= nblk) break;
+      const int j = j_begin + r;
+      // does this column group attend block j, and does it need the element mask
+      bool act, masked;
+      float lr;
+      if constexpr (MODE == DQ_SEL) {
+        act = j == nsel;
+        if (!act) continue;
+        const bool sl = nxt == j;
+        if (sl) {
+          ++ptr;
+          nxt = ptr < topk ? lists[p * topk + ptr] : 0x7fff;
+        }
+        nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+        masked = j == own;
+        lr = sl ? lse2 : INF;
+      } else if constexpr (MODE == DQ_WIN) {
+        act = nvf > 0 && j >= jw_lo && j <= own;
+        if (!act) continue;
+        masked = j == own || j <= jw_edge;
+        lr = lse2;
+      } else {
+        act = nvf > 0 && j * kBlock < nvis_l;
+        if (!act) continue;
+        masked = j * kBlock + kBlock > nvis_f;
+        lr = lse2;
       }
-      nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
       const unsigned char* stage = ring + (size_t)((gi & 1) * GB + qq) * STAGE;
 
       // S^T = K Q^T and dP^T = V dOs^T (K and V fragments in batches of FCH)
@@ -186,10 +230,10 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
         }
       }
 
-      // dS = P (dP - Delta), P from the saved log-sum-exp; causal on the diagonal
-      const float lr = sl ? lse2 : INF;
+      // dS = P (dP - Delta), P from the saved log-sum-exp; element mask on
+      // the causal diagonal / window edge / pooled-key visibility boundary
       FragT dsf[2];
-      if (j != own) {
+      if (!masked) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           float x[8];
@@ -209,7 +253,11 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
           for (int e = 0; e < 8; ++e) {
             const int u = 2 * hf + e / 4, rr = e % 4;
             const int key = j * kBlock + key_of(u, a, rr);
-            const float pr = key <= t ? fast_exp2(st[u][rr] * c1 - lr) : 0.f;
+            bool ok;
+            if constexpr (MODE == DQ_SEL) ok = key <= t;
+            else if constexpr (MODE == DQ_WIN) ok = key <= t && key > t - W;
+            else ok = key < nvis;
+            const float pr = ok ? fast_exp2(st[u][rr] * c1 - lr) : 0.f;
             x[e] = pr * (dp[u][rr] - dl);
           }
           dsf[hf] = Frag<T>::from_f32(x);
@@ -219,60 +267,66 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
       // dq^T += K^T dS^T (K^T fragments in batches)
 #pragma unroll
       for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
-        FragT tf[FCH];
+        FragT tf_[FCH];
 #pragma unroll
-        for (int i = 0; i < FCH; ++i) tf[i] = lds_frag<T>(stage + (size_t)(2 * NFRAG + f0 + i) * FRAG_BYTES, l);
+        for (int i = 0; i < FCH; ++i) tf_[i] = lds_frag<T>(stage + (size_t)(2 * NFRAG + f0 + i) * FRAG_BYTES, l);
 #pragma unroll
         for (int i = 0; i < FCH; ++i)
-          acc[KI::v_mt(f0 + i)] = mma(acc[KI::v_mt(f0 + i)], tf[i], dsf[KI::v_h(f0 + i)]);
+          acc[KI::v_mt(f0 + i)] = mma(acc[KI::v_mt(f0 + i)], tf_[i], dsf[KI::v_h(f0 + i)]);
       }
     }
   }
 
   if (valid) {
-    T* dst = dq + ((size_t)b * s.T + t) * q_row + (size_t)h * D;
+    const size_t o = ((size_t)b * s.T + t) * q_row + (size_t)h * D;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) store4(dst + mt * 16 + 4 * a, acc[mt] * s.scale);
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 r = acc[mt] * s.scale;
+      if (acc_in) r += *reinterpret_cast<const f32x4*>(acc_in + o + mt * 16 + 4 * a);
+      if (acc_out) *reinterpret_cast<f32x4*>(acc_out + o + mt * 16 + 4 * a) = r;
+      if (dq) store4(dq + o + mt * 16 + 4 * a, r);
+    }
   }
 }
 
-template <typename T, int D, int G>
-static hipError_t launch_dq_t(const Shape& s, const void* q, const void* bimg, const int32_t* idx,
-                              const float* lse, const float* delta, const void* dos, void* dq,
-                              hipStream_t st) {
+template <typename T, int D, int G, int MODE>
+static hipError_t launch_dq_t(const Shape& s, const DqArgs& x, hipStream_t st) {
   typedef DqCfg<T, D, G> C;
   const size_t lds = dq_lds_bytes<T, D, G>(s.topk);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, G>,
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, G, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid((s.T + C::P - 1) / C::P * s.Hkv * s.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, G>), grid, dim3(C::NT), lds, st, s, (const T*)q,
-                     (const unsigned char*)bimg, idx, lse, delta, (const T*)dos, (T*)dq);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, G, MODE>), grid, dim3(C::NT), lds, st, s, (const T*)x.q,
+                     (const unsigned char*)x.img, x.indices, x.lse, x.delta, (const T*)x.dos,
+                     x.acc_in, x.acc_out, (T*)x.dq);
   return hipGetLastError();
 }
-template <typename T, int D>
-static hipError_t launch_dq_g(const Shape& s, const void* q, const void* bimg, const int32_t* idx,
-                              const float* lse, const float* delta, const void* dos, void* dq,
-                              hipStream_t st) {
+template <typename T, int D, int MODE>
+static hipError_t launch_dq_g(const Shape& s, const DqArgs& x, hipStream_t st) {
   switch (s.G) {
-    case 1: return launch_dq_t<T, D, 1>(s, q, bimg, idx, lse, delta, dos, dq, st);
-    case 2: return launch_dq_t<T, D, 2>(s, q, bimg, idx, lse, delta, dos, dq, st);
-    case 4: return launch_dq_t<T, D, 4>(s, q, bimg, idx, lse, delta, dos, dq, st);
-    case 8: return launch_dq_t<T, D, 8>(s, q, bimg, idx, lse, delta, dos, dq, st);
-    default: return launch_dq_t<T, D, 16>(s, q, bimg, idx, lse, delta, dos, dq, st);
+    case 1: return launch_dq_t<T, D, 1, MODE>(s, x, st);
+    case 2: return launch_dq_t<T, D, 2, MODE>(s, x, st);
+    case 4: return launch_dq_t<T, D, 4, MODE>(s, x, st);
+    case 8: return launch_dq_t<T, D, 8, MODE>(s, x, st);
+    default: return launch_dq_t<T, D, 16, MODE>(s, x, st);
   }
 }
-
-hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
-                         const int32_t* indices, const float* lse, const float* delta,
-                         const void* dos, void* dq, hipStream_t st) {
+template <int MODE>
+static hipError_t launch_dq_m(bool is_bf16, const Shape& s, const DqArgs& x, hipStream_t st) {
   if (is_bf16) {
-    if (s.D == 64) return launch_dq_g<bf16, 64>(s, q, bimg, indices, lse, delta, dos, dq, st);
-    return launch_dq_g<bf16, 128>(s, q, bimg, indices, lse, delta, dos, dq, st);
+    if (s.D == 64) return launch_dq_g<bf16, 64, MODE>(s, x, st);
+    return launch_dq_g<bf16, 128, MODE>(s, x, st);
   }
-  return launch_dq_g<float, 64>(s, q, bimg, indices, lse, delta, dos, dq, st);
+  return launch_dq_g<float, 64, MODE>(s, x, st);
+}
+
+hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, int mode, const DqArgs& x, hipStream_t st) {
+  if (mode == DQ_WIN) return launch_dq_m<DQ_WIN>(is_bf16, s, x, st);
+  if (mode == DQ_CMP) return launch_dq_m<DQ_CMP>(is_bf16, s, x, st);
+  return launch_dq_m<DQ_SEL>(is_bf16, s, x, st);
 }
 
 }  // namespace nsa

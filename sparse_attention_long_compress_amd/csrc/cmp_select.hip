@@ -14,10 +14,8 @@
 // candidate set 1..c-1.  Query rows are ordered (position, head), 16 rows form
 // one MFMA column group, each wave owns R/NW rows.  Pooled keys and values are
 // staged in LDS 64 blocks at a time (shared by all waves).
-//   Pass 1: S^T = Kc Q^T on MFMA, online softmax, o_cmp = P Vc, and
-//           U = max_j (tau q.Kc_j + tau |q| radius_j) over blocks 0 .. own, an
-//           upper bound of every logit the row's selected blocks can produce
-//           (log2 units).
+//   Pass 1: S^T = Kc Q^T on MFMA, online softmax, o_cmp = P Vc and the
+//           row's log-sum-exp (natural log; -inf when no block is visible).
 //   Pass 2: recompute S^T, p = exp(s - lse), sum p over the G heads of each
 //           position with DPP (adjacent lanes), stage S[position][block] in LDS
 //           64 candidates at a time; each wave scans its share of them with
@@ -71,8 +69,8 @@ struct K2Cfg {
 template <typename T, int D, int G, int LMAX>
 __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
     Shape s, const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ kcl,
-    const T* __restrict__ vct, const float* __restrict__ radius, T* __restrict__ o_cmp,
-    float* __restrict__ ubound, int32_t* __restrict__ indices, int do_topk) {
+    const T* __restrict__ vct, T* __restrict__ o_cmp, float* __restrict__ lse_cmp,
+    int32_t* __restrict__ indices, int do_topk) {
   typedef K2Cfg<T, D, G> C;
   constexpr int P = C::P, CGW = C::CGW, KS = C::KS, MT = C::MT, KST = C::KST, VST = C::VST;
   constexpr int NW = C::NW, NT = C::NT, CPW = C::CPW;
@@ -103,7 +101,6 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   const T* kc_b = kc + (size_t)b * s.nc * kc_row + (size_t)g * D;
   const T* kcl_b = has_lo ? kcl + (size_t)b * s.nc * kc_row + (size_t)g * D : nullptr;
   const T* vct_b = vct + ((size_t)b * s.Hkv + g) * (size_t)D * s.ncp;
-  const float* rad_b = radius ? radius + ((size_t)b * s.Hkv + g) * s.ncp : nullptr;
 
   // stage pooled keys (and the residual) of blocks jb .. jb+63, and optionally
   // the pooled values; rows past the last complete block are clamped (masked)
@@ -141,7 +138,6 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   // rows of this wave: (position, head) with lane column col in group cg
   FragT qf[CGW][KS];
   int tpos[CGW], hidx[CGW], ppos[CGW];
-  float qnorm[CGW];
 #pragma unroll
   for (int cg = 0; cg < CGW; ++cg) {
     const int row = w * C::RWV + cg * 16 + col;
@@ -149,24 +145,17 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
     tpos[cg] = t0 + ppos[cg];
     hidx[cg] = g * G + row % G;
     const T* qrow = q + (((size_t)b * s.T + tpos[cg]) * s.Hq + hidx[cg]) * D;
-    float qn2 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[cg][ks] = Frag<T>::load(qrow + ks * 32 + a * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qn2 += (float)qf[cg][ks][e] * (float)qf[cg][ks][e];
-    }
-    qnorm[cg] = sqrtf(xsum4(qn2));
+    for (int ks = 0; ks < KS; ++ks) qf[cg][ks] = Frag<T>::load(qrow + ks * 32 + a * 8);
   }
 
   // ------------------------------------------------------------------ pass 1
-  float m[CGW], lsum[CGW], ub[CGW], lse2[CGW];
+  float m[CGW], lsum[CGW], lse2[CGW];
   f32x4 o[CGW][MT];
 #pragma unroll
   for (int cg = 0; cg < CGW; ++cg) {
     m[cg] = -INFINITY;
     lsum[cg] = 0.f;
-    ub[cg] = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[cg][mt] = zero4();
   }
@@ -187,10 +176,6 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
             const bool vis = (jj * kBlock + kBlock - 1 <= tpos[cg]) && jj < s.nc;
             const float xv = st[r] * c1;
             x[4 * u + r] = vis ? xv : -INFINITY;
-            // bound over every block the row may select: 0 .. own (complete or
-            // not, all keys of a block lie within its radius of its mean)
-            if (rad_b && jj <= c && jj < s.nc)
-              ub[cg] = fmaxf(ub[cg], xv + qnorm[cg] * c1 * rad_b[jj]);
           }
         }
         float mx = x[0];
@@ -226,10 +211,7 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) store4(orow + mt * 16 + 4 * a, o[cg][mt] * inv);
     }
-    if (ubound) {
-      const float u2 = xmax4(ub[cg]);
-      if (a == 0) ubound[((size_t)b * s.Hq + hidx[cg]) * s.T + tpos[cg]] = u2;
-    }
+    if (lse_cmp && a == 0) lse_cmp[((size_t)b * s.Hq + hidx[cg]) * s.T + tpos[cg]] = lse2[cg] * kLn2;
   }
 
   if (!do_topk) return;
@@ -314,44 +296,43 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
 
 template <typename T, int D, int G>
 static hipError_t launch_cs(const Shape& s, const void* q, const void* kc, const void* kcl,
-                            const void* vct, const float* radius, void* o_cmp, float* ubound,
+                            const void* vct, void* o_cmp, float* lse_cmp,
                             int32_t* indices, bool do_topk, hipStream_t st) {
   constexpr int P = K2Cfg<T, D, G>::P, NT = K2Cfg<T, D, G>::NT;
   dim3 grid(s.T / P * s.Hkv * s.B);
   if (s.topk - 2 <= 16)
     hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 16>), grid, dim3(NT), 0, st, s, (const T*)q,
-                       (const T*)kc, (const T*)kcl, (const T*)vct, radius, (T*)o_cmp, ubound,
+                       (const T*)kc, (const T*)kcl, (const T*)vct, (T*)o_cmp, lse_cmp,
                        indices, do_topk ? 1 : 0);
   else
     hipLaunchKernelGGL((cmp_select_kernel<T, D, G, 32>), grid, dim3(NT), 0, st, s, (const T*)q,
-                       (const T*)kc, (const T*)kcl, (const T*)vct, radius, (T*)o_cmp, ubound,
+                       (const T*)kc, (const T*)kcl, (const T*)vct, (T*)o_cmp, lse_cmp,
                        indices, do_topk ? 1 : 0);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_cs_g(const Shape& s, const void* q, const void* kc, const void* kcl,
-                              const void* vct, const float* radius, void* o_cmp, float* ubound,
+                              const void* vct, void* o_cmp, float* lse_cmp,
                               int32_t* indices, bool do_topk, hipStream_t st) {
   switch (s.G) {
-    case 1: return launch_cs<T, D, 1>(s, q, kc, kcl, vct, radius, o_cmp, ubound, indices, do_topk, st);
-    case 2: return launch_cs<T, D, 2>(s, q, kc, kcl, vct, radius, o_cmp, ubound, indices, do_topk, st);
-    case 4: return launch_cs<T, D, 4>(s, q, kc, kcl, vct, radius, o_cmp, ubound, indices, do_topk, st);
-    case 8: return launch_cs<T, D, 8>(s, q, kc, kcl, vct, radius, o_cmp, ubound, indices, do_topk, st);
-    default: return launch_cs<T, D, 16>(s, q, kc, kcl, vct, radius, o_cmp, ubound, indices, do_topk, st);
+    case 1: return launch_cs<T, D, 1>(s, q, kc, kcl, vct, o_cmp, lse_cmp, indices, do_topk, st);
+    case 2: return launch_cs<T, D, 2>(s, q, kc, kcl, vct, o_cmp, lse_cmp, indices, do_topk, st);
+    case 4: return launch_cs<T, D, 4>(s, q, kc, kcl, vct, o_cmp, lse_cmp, indices, do_topk, st);
+    case 8: return launch_cs<T, D, 8>(s, q, kc, kcl, vct, o_cmp, lse_cmp, indices, do_topk, st);
+    default: return launch_cs<T, D, 16>(s, q, kc, kcl, vct, o_cmp, lse_cmp, indices, do_topk, st);
   }
 }
 
 hipError_t launch_cmp_select(bool is_bf16, const Shape& s, const void* q, const void* kc,
-                             const void* kc_lo, const void* vct, const float* radius,
-                             void* o_cmp, float* ubound, int32_t* indices, bool do_topk,
-                             hipStream_t st) {
+                             const void* kc_lo, const void* vct, void* o_cmp, float* lse_cmp,
+                             int32_t* indices, bool do_topk, hipStream_t st) {
   if (is_bf16) {
     if (s.D == 64)
-      return launch_cs_g<bf16, 64>(s, q, kc, kc_lo, vct, radius, o_cmp, ubound, indices, do_topk, st);
-    return launch_cs_g<bf16, 128>(s, q, kc, kc_lo, vct, radius, o_cmp, ubound, indices, do_topk, st);
+      return launch_cs_g<bf16, 64>(s, q, kc, kc_lo, vct, o_cmp, lse_cmp, indices, do_topk, st);
+    return launch_cs_g<bf16, 128>(s, q, kc, kc_lo, vct, o_cmp, lse_cmp, indices, do_topk, st);
   }
-  return launch_cs_g<float, 64>(s, q, kc, nullptr, vct, radius, o_cmp, ubound, indices, do_topk, st);
+  return launch_cs_g<float, 64>(s, q, kc, nullptr, vct, o_cmp, lse_cmp, indices, do_topk, st);
 }
 
 }  // namespace nsa

@@ -24,48 +24,93 @@ hipError_t launch_pool(bool is_bf16, const Shape& s, const void* k, const void* 
                        hipStream_t st);
 
 // K2: compressed attention + importance + top-k.
-//   o_cmp [B][T][Hq][D] (nullable), ubound [B][Hq][T] (nullable; log2 units),
-//   indices [B][Hkv][T][topk] (written unless do_topk == false).
+//   o_cmp [B][T][Hq][D] (nullable), lse_cmp [B][Hq][T] fp32 natural log, -inf
+//   where no compressed block is visible (nullable), indices
+//   [B][Hkv][T][topk] (written unless do_topk == false).
 hipError_t launch_cmp_select(bool is_bf16, const Shape& s, const void* q, const void* kc,
-                             const void* kc_lo, const void* vct, const float* radius,
-                             void* o_cmp, float* ubound, int32_t* indices, bool do_topk,
-                             hipStream_t st);
+                             const void* kc_lo, const void* vct, void* o_cmp, float* lse_cmp,
+                             int32_t* indices, bool do_topk, hipStream_t st);
 
 // K3: selection + window + gated combine.  knorm from K1 (required).
+//   lse / o_sel: selection branch log-sum-exp [B][Hq][T] and output (nullable);
+//   lse_win / o_win: the same for the window branch (nullable).
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
                           const void* kvimg, const void* gates, const void* o_cmp,
                           const float* knorm, const int32_t* indices, void* out, float* lse,
-                          void* o_sel, hipStream_t st);
+                          void* o_sel, float* lse_win, void* o_win, hipStream_t st);
 
 // Backward (selection branch).
 //   prep: bimg [B][Hkv][T/64][BwdImage<T, D>::BYTES] (K, V, K^T fragments of
 //   each key block), delta [B][Hq][T] fp32, dos [B][T][Hq][D].
+// Extra outputs of the preparation kernel for the full backward (all
+// [B][T][Hq][D] in the input dtype or [B][Hq][T] fp32; dgates [B][T][Hq][3]).
+struct PrepFullArgs {
+  const void* o_win;
+  const void* o_cmp;
+  void* dos_w;
+  void* dos_c;
+  float* delta_w;
+  float* delta_c;
+  void* dgates;
+};
 hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* v,
                            const void* gates, const void* o_sel, const void* dout, void* bimg,
-                           float* delta, void* dos, hipStream_t st);
+                           float* delta, void* dos, const PrepFullArgs* full, hipStream_t st);
+// pooled-key images [B][Hkv][ceil(nc / 64)][BwdImage<T, D>::BYTES]
+hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* k, const void* v,
+                                 void* pimg, hipStream_t st);
 hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* revmap,
                              hipStream_t st);
-hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, const void* q, const void* bimg,
-                         const int32_t* indices, const float* lse, const float* delta,
-                         const void* dos, void* dq, hipStream_t st);
+// dq pass of one branch (mode 0 selection, 1 window, 2 compression over the
+// pooled-key images).  img: block images (modes 0, 1) or pooled-key images
+// (mode 2); indices only for mode 0; lse / delta [B][Hq][T] and dos
+// [B][T][Hq][D] of that branch.  The pass adds tau * its gradient to acc_in
+// (fp32 [B][T][Hq][D], nullable) and writes the sum to acc_out (fp32,
+// nullable) and / or dq (input dtype, nullable).
+struct DqArgs {
+  const void* q;
+  const void* img;
+  const int32_t* indices;
+  const float* lse;
+  const float* delta;
+  const void* dos;
+  const float* acc_in;
+  float* acc_out;
+  void* dq;
+};
+hipError_t launch_bwd_dq(bool is_bf16, const Shape& s, int mode, const DqArgs& args, hipStream_t st);
+
 // Planning and partial-sum buffers of the dk/dv pass (all in the workspace):
 //   lists [B][Hkv][nblk][T] u16 positions that selected each block, counts
 //   [B][Hkv][nblk], items (bwd_items_bytes), slot_base / slot_cnt
-//   [B][Hkv][nblk], nitems (1 int), part (bwd_part_floats fp32).
+//   [B][Hkv][nblk], slot_base_c / slot_cnt_c [B][Hkv][ceil(nc / 64)] (full
+//   backward only), nitems (1 int), part (bwd_part_floats fp32).
 struct BwdPlanWs {
   void* items;
   uint16_t* lists;
   int* counts;
   int* slot_base;
   int* slot_cnt;
+  int* slot_base_c;
+  int* slot_cnt_c;
   int* nitems;
   float* part;
 };
-hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const void* q, const void* bimg,
-                           const float* lse, const float* delta, const void* dos,
-                           const uint64_t* revmap, void* dk, void* dv, const BwdPlanWs& ws,
-                           hipStream_t st);
-size_t bwd_items_bytes(const Shape& s);
-size_t bwd_part_floats(const Shape& s);
+// The branches a dk/dv pass covers: selection only (full == false; index 0 of
+// lse / delta / dos) or selection, window and compression (indices 0, 1, 2).
+// img: block images; pimg: pooled-key images (full only).
+struct KvBranches {
+  bool full;
+  const void* q;
+  const void* img;
+  const void* pimg;
+  const float* lse[3];
+  const float* delta[3];
+  const void* dos[3];
+};
+hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const KvBranches& br, const uint64_t* revmap,
+                           void* dk, void* dv, const BwdPlanWs& ws, hipStream_t st);
+size_t bwd_items_bytes(const Shape& s, bool full);
+size_t bwd_part_floats(const Shape& s, bool full);
 
 }  // namespace nsa

@@ -81,6 +81,8 @@ struct SelWinArgs {
   void* out;
   float* lse;
   void* o_sel;
+  float* lse_win;
+  void* o_win;
 };
 
 template <typename T, int D, int G>
@@ -503,12 +505,14 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
     const float gs = sel_on ? to_f32(grow[1]) : 0.f;
     const float gw = win_on ? to_f32(grow[2]) : 0.f;
     const float iw = win_on ? gw / lw : 0.f;
+    const float ilw = win_on ? 1.f / lw : 0.f;
     const float il = need_sel ? 1.f / ls : 0.f;
     const size_t obase = ((size_t)b * s.T + t) * q_row + (size_t)h * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int d0 = mt * 16 + 4 * a;
       f32x4 res = acc_w[cg][mt] * iw;
+      if (args.o_win) store4((T*)args.o_win + obase + d0, acc_w[cg][mt] * ilw);
       if (need_sel) {
         const f32x4 os = acc_s[cg][mt] * il;
         if (sel_on) res += os * gs;
@@ -518,6 +522,8 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
       store4(out + obase + d0, res);
     }
     if (args.lse && a == 0) args.lse[((size_t)b * s.Hq + h) * s.T + t] = (mr_s[cg] + __log2f(ls)) * kLn2;
+    if (args.lse_win && a == 0)
+      args.lse_win[((size_t)b * s.Hq + h) * s.T + t] = win_on ? (mr_w[cg] + __log2f(lw)) * kLn2 : -INF;
   }
 }
 
@@ -549,8 +555,8 @@ static hipError_t launch_sw_g(const Shape& s, const SelWinArgs& a, hipStream_t s
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
                           const void* kvimg, const void* gates, const void* o_cmp,
                           const float* knorm, const int32_t* indices, void* out, float* lse,
-                          void* o_sel, hipStream_t st) {
-  SelWinArgs a{q, k, kvimg, gates, o_cmp, knorm, indices, out, lse, o_sel};
+                          void* o_sel, float* lse_win, void* o_win, hipStream_t st) {
+  SelWinArgs a{q, k, kvimg, gates, o_cmp, knorm, indices, out, lse, o_sel, lse_win, o_win};
   if (is_bf16) {
     if (s.D == 64) return launch_sw_g<bf16, 64>(s, a, st);
     return launch_sw_g<bf16, 128>(s, a, st);
