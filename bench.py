@@ -62,6 +62,14 @@ def useful_bwd_flops(wl):
     return 10 * wl.head_dim * wl.batch * wl.n_q_heads * sel
 
 
+def useful_full_bwd_flops(wl):
+    """Gradient of all three branches: 10 D FLOPs per (query, head, attended key)
+    over the selected, window and visible pooled keys (the pooled keys' gradient
+    back through the mean-pool is not counted)."""
+    sel, win, cmp = useful_counts(wl)
+    return 10 * wl.head_dim * wl.batch * wl.n_q_heads * (sel + win + cmp)
+
+
 def algorithmic_bytes(wl):
     """HBM bytes the whole forward must move at least once (inputs read once,
     output written once)."""
@@ -196,7 +204,9 @@ def main():
                     help="print the traffic summary of sel_win_kernel from rocprofv3 CSVs and exit")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
     ap.add_argument("--no-backward", action="store_true",
-                    help="time the forward only (the selection-branch backward is timed by default)")
+                    help="time the forward only (the selection-branch backward and a training "
+                         "step -- forward with saved tensors plus the full backward -- are timed "
+                         "by default)")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary, copy_bytes=args.copy_bytes, kernel="sel_win_kernel"))
@@ -275,6 +285,35 @@ def main():
         torch.cuda.synchronize()
         bwd = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])) * 1e-3
 
+    # a training step: the forward that saves every tensor the full backward
+    # needs, then the gradient of all three branches and the gates
+    train = None
+    if not args.no_backward:
+        wsf = nsa.alloc_workspace(p, dev["q"].device, backward="full")
+        saved = nsa.forward_train(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                                  window=wl.window, scale=wl.scale, workspace=ws)
+        fgrads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]),
+                  torch.empty_like(dev["gates"]))
+
+        def tstep(e):
+            e[0].record()
+            nsa.forward_train(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                              window=wl.window, scale=wl.scale, workspace=ws, out=saved["out"])
+            e[1].record()
+            nsa.backward(dev["q"], dev["k"], dev["v"], dev["gates"], saved, dev["dout"],
+                         top_k=wl.top_k, window=wl.window, scale=wl.scale, workspace=wsf,
+                         out=fgrads)
+            e[2].record()
+
+        tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.warmup + args.steps)]
+        for i in range(args.warmup + args.steps):
+            tstep(tev[i])
+        torch.cuda.synchronize()
+        tev = tev[args.warmup:]
+        train = (float(np.mean([e[0].elapsed_time(e[1]) for e in tev])) * 1e-3,
+                 float(np.mean([e[1].elapsed_time(e[2]) for e in tev])) * 1e-3)
+
     k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
     k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
     k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
@@ -284,7 +323,9 @@ def main():
     if args.profile_only:
         print(json.dumps({"profile_only": True, "ms_per_step": wall * 1e3,
                           "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6,
-                          "sel_bwd_us": None if bwd is None else bwd * 1e6}), flush=True)
+                          "sel_bwd_us": None if bwd is None else bwd * 1e6,
+                          "train_fwd_us": None if train is None else train[0] * 1e6,
+                          "full_bwd_us": None if train is None else train[1] * 1e6}), flush=True)
         return
 
     achieved = fl["sel_win"] / k3 / 1e12
@@ -321,6 +362,14 @@ def main():
             "pct_bf16_peak": round(100 * fb / bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
             "fwd_plus_bwd_ms": round((wall + bwd) * 1e3, 4),
             "fwd_plus_bwd_tokens_per_s": round(tokens / (wall + bwd), 1)}
+    if train is not None:
+        ff, fbf = fl["total"], useful_full_bwd_flops(wl)
+        step_s = train[0] + train[1]
+        res["training_step"] = {
+            "forward_us": round(train[0] * 1e6, 2), "full_backward_us": round(train[1] * 1e6, 2),
+            "full_backward_useful_tflops": round(fbf / train[1] / 1e12, 2),
+            "step_ms": round(step_s * 1e3, 4), "tokens_per_s": round(tokens / step_s, 1),
+            "pct_bf16_peak": round(100 * (ff + fbf) / step_s / 1e12 / PEAK_BF16_TFLOPS, 2)}
     if not args.no_cpu_baseline:
         f64 = {k: as_f64(v) for k, v in cpu.items()}
         res["cpu_baseline"] = cpu_baseline(wl, f64)

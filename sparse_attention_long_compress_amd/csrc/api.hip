@@ -74,7 +74,7 @@ FwdLayout fwd_layout(const Shape& s, size_t es) {
 // Backward workspace regions (full: all three branches, nsa_backward).
 struct BwdLayout {
   size_t bimg, delta, dos, revmap, lists, counts, items, slot_base, slot_cnt, nitems, part;
-  size_t pimg, dos_w, dos_c, delta_w, delta_c, dq32, slot_base_c, slot_cnt_c, total;
+  size_t pimg, kc, vc, dos_w, dos_c, delta_w, delta_c, dq32, slot_base_c, slot_cnt_c, total;
 };
 BwdLayout bwd_layout(const Shape& s, size_t es, bool full) {
   BwdLayout L;
@@ -93,9 +93,12 @@ BwdLayout bwd_layout(const Shape& s, size_t es, bool full) {
   L.slot_cnt = o;  o += up(NJ * 4, kAlign);
   L.nitems = o;    o += up(4, kAlign);
   L.part = o;      o += up(nsa::bwd_part_floats(s, full) * 4, kAlign);
-  L.pimg = L.dos_w = L.dos_c = L.delta_w = L.delta_c = L.dq32 = L.slot_base_c = L.slot_cnt_c = 0;
+  L.pimg = L.kc = L.vc = L.dos_w = L.dos_c = L.delta_w = L.delta_c = L.dq32 = 0;
+  L.slot_base_c = L.slot_cnt_c = 0;
   if (full) {
     L.pimg = o;        o += up(NJc * 3 * 64 * s.D * es, kAlign);
+    L.kc = o;          o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
+    L.vc = o;          o += up((size_t)s.B * s.nc * s.Hkv * s.D * es, kAlign);
     L.dos_w = o;       o += up(elems * es, kAlign);
     L.dos_c = o;       o += up(elems * es, kAlign);
     L.delta_w = o;     o += up(rows * 4, kAlign);
@@ -351,7 +354,9 @@ nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const voi
   hipError_t e = nsa::launch_bwd_prep(bf, s, k, v, gates, sv->o_sel, dout, ws + L.bimg,
                                       (float*)(ws + L.delta), ws + L.dos, &fx, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
-  e = nsa::launch_bwd_pool_image(bf, s, k, v, ws + L.pimg, hs);
+  e = nsa::launch_pool(bf, s, k, v, ws + L.kc, ws + L.vc, nullptr, nullptr, nullptr, nullptr, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_pool_image(bf, s, ws + L.kc, ws + L.vc, ws + L.pimg, hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;
   e = nsa::launch_bwd_revmap(s, sv->indices, (uint64_t*)(ws + L.revmap), hs);
   if (e != hipSuccess) return NSA_ERR_LAUNCH;

@@ -169,31 +169,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
 
 // Backward image of the pooled keys: grid (ceil(nc / 64), Hkv, B), 256
 // threads; pooled "block" J holds the pooled keys / values 64 J .. 64 J + 63
-// (the mean of the 64 tokens of each block, rounded once to T; zero past the
-// last complete block) in the BwdImage layout, so the backward kernels treat
-// the compressed branch's keys like a key block.
+// (kc, vc [B][nc][Hkv][D] from the pooling kernel; zero past the last
+// complete block) in the BwdImage layout, so the backward kernels treat the
+// compressed branch's keys like a key block.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pool_image_kernel(Shape s, const T* __restrict__ k,
-                                                             const T* __restrict__ v,
+__global__ __launch_bounds__(256) void bwd_pool_image_kernel(Shape s, const T* __restrict__ kc,
+                                                             const T* __restrict__ vc,
                                                              unsigned char* __restrict__ pimg) {
   typedef BwdImage<T, D> I;
+  constexpr int EPV = 16 / sizeof(T);
+  typedef typename V16b<T>::type Vec;
   __shared__ __align__(16) T kt[kBlock][D + 8];
   __shared__ __align__(16) T vt[kBlock][D + 8];
   const int J = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const size_t k_row = (size_t)s.Hkv * D;
-  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
-    const int r = i / D, d = i % D;
-    const int jj = J * kBlock + r;  // pooled key = block jj of tokens
-    float sk = 0.f, sv = 0.f;
+  for (int i = threadIdx.x; i < kBlock * (D / EPV); i += 256) {
+    const int r = i / (D / EPV), c8 = i % (D / EPV);
+    const int jj = J * kBlock + r;
+    Vec kv_, vv_;
     if (jj < s.nc) {
-      const size_t src = ((size_t)b * s.T + (size_t)jj * kBlock) * k_row + (size_t)g * D + d;
-      for (int tt = 0; tt < kBlock; ++tt) {
-        sk += (float)k[src + (size_t)tt * k_row];
-        sv += (float)v[src + (size_t)tt * k_row];
-      }
+      const size_t src = ((size_t)b * s.nc + jj) * k_row + (size_t)g * D + c8 * EPV;
+      kv_ = *reinterpret_cast<const Vec*>(kc + src);
+      vv_ = *reinterpret_cast<const Vec*>(vc + src);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) { kv_[e] = (T)0.f; vv_[e] = (T)0.f; }
     }
-    kt[r][d] = (T)(sk * (1.f / kBlock));
-    vt[r][d] = (T)(sv * (1.f / kBlock));
+    *reinterpret_cast<Vec*>(&kt[r][c8 * EPV]) = kv_;
+    *reinterpret_cast<Vec*>(&vt[r][c8 * EPV]) = vv_;
   }
   __syncthreads();
   const int NJc = (s.nc + kBlock - 1) / kBlock;
@@ -248,20 +251,20 @@ hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* k, const void* v,
+hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* kc, const void* vc,
                                  void* pimg, hipStream_t st) {
   dim3 grid((s.nc + kBlock - 1) / kBlock, s.Hkv, s.B);
   unsigned char* im = (unsigned char*)pimg;
   if (is_bf16) {
     if (s.D == 64)
       hipLaunchKernelGGL((bwd_pool_image_kernel<bf16, 64>), grid, dim3(256), 0, st, s,
-                         (const bf16*)k, (const bf16*)v, im);
+                         (const bf16*)kc, (const bf16*)vc, im);
     else
       hipLaunchKernelGGL((bwd_pool_image_kernel<bf16, 128>), grid, dim3(256), 0, st, s,
-                         (const bf16*)k, (const bf16*)v, im);
+                         (const bf16*)kc, (const bf16*)vc, im);
   } else {
     hipLaunchKernelGGL((bwd_pool_image_kernel<float, 64>), grid, dim3(256), 0, st, s,
-                       (const float*)k, (const float*)v, im);
+                       (const float*)kc, (const float*)vc, im);
   }
   return hipGetLastError();
 }

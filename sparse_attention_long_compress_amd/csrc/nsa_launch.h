@@ -56,8 +56,9 @@ struct PrepFullArgs {
 hipError_t launch_bwd_prep(bool is_bf16, const Shape& s, const void* k, const void* v,
                            const void* gates, const void* o_sel, const void* dout, void* bimg,
                            float* delta, void* dos, const PrepFullArgs* full, hipStream_t st);
-// pooled-key images [B][Hkv][ceil(nc / 64)][BwdImage<T, D>::BYTES]
-hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* k, const void* v,
+// pooled-key images [B][Hkv][ceil(nc / 64)][BwdImage<T, D>::BYTES] from the
+// pooled keys / values kc, vc [B][nc][Hkv][D]
+hipError_t launch_bwd_pool_image(bool is_bf16, const Shape& s, const void* kc, const void* vc,
                                  void* pimg, hipStream_t st);
 hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* revmap,
                              hipStream_t st);
