@@ -203,6 +203,9 @@ def main():
                                                        "COPY_WRITE_CSV"),
                     help="print the traffic summary of sel_win_kernel from rocprofv3 CSVs and exit")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    ap.add_argument("--ab-single", action="store_true",
+                    help="only time the two-pass selection backward against the single-pass one "
+                         "with atomics (nsa_select_bwd_single) and print one JSON line")
     ap.add_argument("--no-backward", action="store_true",
                     help="time the forward only (the selection-branch backward and a training "
                          "step -- forward with saved tensors plus the full backward -- are timed "
@@ -234,6 +237,33 @@ def main():
     p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale)
     ws = nsa.alloc_workspace(p, dev["q"].device)
     out = torch.empty_like(dev["q"])
+
+    if args.ab_single:
+        res_f = nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                            window=wl.window, scale=wl.scale, workspace=ws, want_indices=True,
+                            want_lse=True, want_o_sel=True)
+        fargs = (dev["q"], dev["k"], dev["v"], dev["gates"], res_f["indices"], res_f["lse_sel"],
+                 res_f["o_sel"], dev["dout"])
+        grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]))
+        ab = {}
+        for name, fn, mode in (("two_pass", nsa.select_bwd, True),
+                               ("single_pass_atomic", nsa.select_bwd_single, "single")):
+            wsx = nsa.alloc_workspace(p, dev["q"].device, backward=mode)
+            for _ in range(args.warmup):
+                fn(*fargs, top_k=wl.top_k, scale=wl.scale, workspace=wsx, out=grads)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn(*fargs, top_k=wl.top_k, scale=wl.scale, workspace=wsx, out=grads)
+            e1.record()
+            torch.cuda.synchronize()
+            ab[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
+            del wsx
+        ab["single_over_two_pass"] = round(ab["single_pass_atomic_us"] / ab["two_pass_us"], 2)
+        print(json.dumps({"selection_backward_ab": ab, "workload": wl.name, "steps": args.steps}),
+              flush=True)
+        return
 
     def step(events=None):
         nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,

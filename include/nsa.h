@@ -115,8 +115,8 @@ const char* nsa_status_string(nsa_status_t status);
 nsa_status_t nsa_check_params(const nsa_params_t* p);
 
 /* Bytes of device workspace needed by nsa_forward / nsa_forward_train
- * (for_backward = 0), by nsa_select_bwd (for_backward = 1) or by nsa_backward
- * (for_backward = 2).  Returns 0 for invalid params.  The size is monotone in
+ * (for_backward = 0), by nsa_select_bwd (for_backward = 1), by nsa_backward
+ * (for_backward = 2) or by nsa_select_bwd_single (for_backward = 3).  Returns 0 for invalid params.  The size is monotone in
  * seq_len and batch. */
 size_t nsa_workspace_size(const nsa_params_t* p, int for_backward);
 
@@ -172,6 +172,17 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
                             const int32_t* indices, const float* lse_sel, const void* o_sel,
                             const void* dout, const nsa_params_t* p, void* dq, void* dk,
                             void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* The same gradient as nsa_select_bwd in ONE query-stationary pass that adds
+ * dk and dv with fp32 atomics ([SIC] Method: the single-pass kernel whose
+ * atomic contention motivates the two-pass scheme; kept for that A/B
+ * comparison).  Same arguments and results up to the order of the fp32
+ * additions (not bitwise reproducible).  bf16 only (NSA_ERR_UNSUPPORTED
+ * otherwise).  workspace: at least nsa_workspace_size(p, 3) bytes. */
+nsa_status_t nsa_select_bwd_single(const void* q, const void* k, const void* v, const void* gates,
+                                   const int32_t* indices, const float* lse_sel, const void* o_sel,
+                                   const void* dout, const nsa_params_t* p, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Tensors the full backward reads, written by nsa_forward_train.  All device
  * pointers, 16-byte aligned, owned by the caller:

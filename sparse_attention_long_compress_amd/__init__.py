@@ -20,7 +20,7 @@ SKIP_CMP_OUT, SKIP_SEL, SKIP_WIN, INDICES_IN = 1, 2, 4, 8
 EXPORTED = (
     "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_workspace_size",
     "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
-    "nsa_forward_train", "nsa_backward",
+    "nsa_forward_train", "nsa_backward", "nsa_select_bwd_single",
 )
 
 
@@ -78,6 +78,8 @@ def lib():
         L.nsa_select_bwd.argtypes = [vp, vp, vp, vp, i32p, f32p, vp, vp, P, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
         L.nsa_select_bwd.restype = ctypes.c_int
+        L.nsa_select_bwd_single.argtypes = L.nsa_select_bwd.argtypes
+        L.nsa_select_bwd_single.restype = ctypes.c_int
         S = ctypes.POINTER(NsaSaved)
         L.nsa_forward_train.argtypes = [vp, vp, vp, vp, P, vp, S, vp, ctypes.c_size_t, vp]
         L.nsa_forward_train.restype = ctypes.c_int
@@ -137,8 +139,9 @@ def params_for(q, k, *, top_k, window, scale=None, flags=0):
 
 
 def workspace_size(p: NsaParams, backward=False) -> int:
-    """backward: False (forward), True (selection backward) or "full" (nsa_backward)."""
-    mode = 2 if backward == "full" else (1 if backward else 0)
+    """backward: False (forward), True (selection backward), "full" (nsa_backward)
+    or "single" (nsa_select_bwd_single)."""
+    mode = {"full": 2, "single": 3}.get(backward, 1 if backward else 0)
     return int(lib().nsa_workspace_size(ctypes.byref(p), mode))
 
 
@@ -284,3 +287,21 @@ def backward(q, k, v, gates, saved, dout, *, top_k, window, scale=None, workspac
                               ctypes.byref(p), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws),
                               ws.numel(), _stream(stream)), "nsa_backward")
     return dq, dk, dv, dg
+
+
+def select_bwd_single(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, scale=None,
+                      workspace=None, stream=None, out=None):
+    """(dq, dk, dv) of the selection branch in one query-stationary pass with
+    fp32 atomics (nsa_select_bwd_single; bf16 only, not bitwise reproducible)."""
+    torch = _torch()
+    p = params_for(q, k, top_k=top_k, window=1, scale=scale)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device, backward="single")
+    if out is not None:
+        dq, dk, dv = out
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib().nsa_select_bwd_single(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(indices),
+                                       _ptr(lse_sel), _ptr(o_sel), _ptr(dout), ctypes.byref(p),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "nsa_select_bwd_single")
+    return dq, dk, dv

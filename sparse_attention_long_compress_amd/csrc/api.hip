@@ -155,6 +155,8 @@ size_t nsa_workspace_size(const nsa_params_t* p, int for_backward) {
   if (check(p) != NSA_OK) return 0;
   const Shape s = make_shape(p);
   if (for_backward == 2) return bwd_layout(s, esize(p), true).total;
+  if (for_backward == 3)  // single-pass selection backward: + fp32 dk, dv accumulators
+    return bwd_layout(s, esize(p), false).total + 2 * up((size_t)s.B * s.T * s.Hkv * s.D * 4, kAlign);
   return for_backward ? bwd_layout(s, esize(p), false).total : fwd_layout(s, esize(p)).total;
 }
 
@@ -321,6 +323,36 @@ nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const v
                      {(const float*)(ws + L.delta), nullptr, nullptr},
                      {ws + L.dos, nullptr, nullptr}};
   e = nsa::launch_bwd_dkdv(bf, s, br, (const uint64_t*)(ws + L.revmap), dk, dv, plan_ws(ws, L), hs);
+  return launched(e);
+}
+
+nsa_status_t nsa_select_bwd_single(const void* q, const void* k, const void* v, const void* gates,
+                                   const int32_t* indices, const float* lse_sel, const void* o_sel,
+                                   const void* dout, const nsa_params_t* p, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (p->dtype != NSA_BF16) return NSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !gates || !indices || !lse_sel || !o_sel || !dout || !dq || !dk || !dv)
+    return NSA_ERR_NULL;
+  if (!workspace) return NSA_ERR_WORKSPACE;
+  const Shape s = make_shape(p);
+  const size_t es = esize(p);
+  const BwdLayout L = bwd_layout(s, es, false);
+  const size_t acc = up((size_t)s.B * s.T * s.Hkv * s.D * 4, kAlign);
+  if (ws_bytes < L.total + 2 * acc) return NSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gates) || !aligned16(indices) ||
+      !aligned16(lse_sel) || !aligned16(o_sel) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)workspace % kAlign) != 0)
+    return NSA_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = nsa::launch_bwd_prep(true, s, k, v, gates, o_sel, dout, ws + L.bimg,
+                                      (float*)(ws + L.delta), ws + L.dos, nullptr, hs);
+  if (e != hipSuccess) return NSA_ERR_LAUNCH;
+  e = nsa::launch_bwd_single(s, q, ws + L.bimg, indices, lse_sel, (const float*)(ws + L.delta),
+                             ws + L.dos, dq, dk, dv, (float*)(ws + L.total),
+                             (float*)(ws + L.total + acc), hs);
   return launched(e);
 }
 

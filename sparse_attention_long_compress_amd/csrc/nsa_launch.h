@@ -114,4 +114,11 @@ hipError_t launch_bwd_dkdv(bool is_bf16, const Shape& s, const KvBranches& br, c
 size_t bwd_items_bytes(const Shape& s, bool full);
 size_t bwd_part_floats(const Shape& s, bool full);
 
+// Single-pass selection backward with atomics (bf16): dq written directly;
+// dk, dv accumulated in fp32 (dk32, dv32 [B][T][Hkv][D], zeroed here) by
+// atomic adds, then rounded into dk (x tau) and dv.
+hipError_t launch_bwd_single(const Shape& s, const void* q, const void* bimg, const int32_t* indices,
+                             const float* lse, const float* delta, const void* dos, void* dq, void* dk,
+                             void* dv, float* dk32, float* dv32, hipStream_t st);
+
 }  // namespace nsa

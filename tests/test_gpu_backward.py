@@ -112,3 +112,25 @@ def test_select_bwd_32k_on_a_2048_slice():
     assert torch.equal(d_full, d_pre)
     for nm, g_, r_ in zip(("dq", "dk", "dv"), got_pre, ref_pre):
         grad_close(to_np(g_), r_, wl.dtype, nm + "@2048")
+
+
+SINGLE_CASES = [
+    ("340m-gqa4", 1024, {}),
+    ("1b3-gqa4", 1024, {"batch": 1}),
+    ("340m-gqa4", 512, {"n_q_heads": 4, "n_kv_heads": 4}),                # G = 1
+    ("1b3-gqa4", 512, {"batch": 1, "n_q_heads": 16, "n_kv_heads": 2}),    # G = 8
+    ("340m-gqa4", 640, {"top_k": 3}),
+]
+
+
+@pytest.mark.parametrize("name,T,over", SINGLE_CASES)
+def test_single_pass_atomic_backward_matches_oracle(name, T, over):
+    # the one-pass alternative (dk / dv by fp32 atomics) at the same bounds
+    wl = WORKLOADS[name].with_(**over)
+    print("case", name, T, over, flush=True)
+    _, ref, dev, idx, fwd = run_both(wl, T)
+    got = nsa.select_bwd_single(dev["q"], dev["k"], dev["v"], dev["gates"], idx, fwd["lse_sel"],
+                                fwd["o_sel"], dev["dout"], top_k=wl.top_k, scale=wl.scale)
+    torch.cuda.synchronize()
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        grad_close(to_np(g_), r_, wl.dtype, nm)
