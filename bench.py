@@ -110,8 +110,23 @@ def cpu_baseline(wl, arrs_f64, min_seconds=10.0, max_passes=50):
 # --- HBM traffic of the dominant kernel from committed rocprofv3 counters -----
 PROFILES = os.path.join(ROOT, "profiles")
 K3_SOURCES = ["sparse_attention_long_compress_amd/csrc/sel_win.hip",
+              "sparse_attention_long_compress_amd/csrc/sel_compact.hip",
               "sparse_attention_long_compress_amd/csrc/nsa_device.h",
               "sparse_attention_long_compress_amd/csrc/nsa_launch.h"]
+
+
+def k3_kernel(wl):
+    """Name of the selection/window kernel the library runs for this workload:
+    the packed-selection kernel covers bf16, head_dim 64, four query heads per
+    KV group, a window of at most 30 blocks and its LDS budget (sequences up to
+    8832); every other shape runs the general kernel."""
+    G = wl.n_q_heads // wl.n_kv_heads
+    nb = -(-wl.seq_len // 64)
+    lds = 159856 + 8 * nb
+    if (wl.dtype == "bf16" and wl.head_dim == 64 and G == 4 and (wl.window - 1) // 64 + 2 <= 32
+            and lds <= 160 * 1024):
+        return "sel_compact_kernel"
+    return "sel_win_kernel"
 
 
 def kernel_source_hash(paths=K3_SOURCES):
@@ -135,10 +150,10 @@ def read_summary(path):
     return out
 
 
-def committed_traffic(workload):
-    """Bytes per launch of sel_win_kernel from profiles/, or None when the
-    summary is missing or the kernel source changed since it was taken."""
-    summ = read_summary(os.path.join(PROFILES, f"sel_win_kernel_{workload}_traffic.txt"))
+def committed_traffic(workload, kernel):
+    """Bytes per launch of the selection/window kernel from profiles/, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    summ = read_summary(os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt"))
     if not summ or summ.get("source_hash") != kernel_source_hash():
         return None
     try:
@@ -201,7 +216,8 @@ def main():
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                        "COPY_WRITE_CSV"),
-                    help="print the traffic summary of sel_win_kernel from rocprofv3 CSVs and exit")
+                    help="print the traffic summary of the workload's selection/window kernel "
+                         "from rocprofv3 CSVs and exit")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
     ap.add_argument("--ab-single", action="store_true",
                     help="only time the two-pass selection backward against the single-pass one "
@@ -212,7 +228,9 @@ def main():
                          "by default)")
     args = ap.parse_args()
     if args.pmc_summary:
-        print(pmc_summary(*args.pmc_summary, copy_bytes=args.copy_bytes, kernel="sel_win_kernel"))
+        from sparse_attention_long_compress_amd.synth import WORKLOADS as _W
+        print(pmc_summary(*args.pmc_summary, copy_bytes=args.copy_bytes,
+                          kernel=k3_kernel(_W[args.workload])))
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -380,10 +398,10 @@ def main():
         "pct_bf16_peak": round(100 * fl["total"] / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "stage_us": {"pool": round(k1 * 1e6, 2), "cmp_select": round(k2 * 1e6, 2),
                      "sel_win_combine": round(k3 * 1e6, 2), "events_total": round(ev_step * 1e6, 2)},
-        "roofline": {"kernel": "sel_win_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": k3_kernel(wl), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": committed_traffic(wl.name)},
+                     "traffic": committed_traffic(wl.name, k3_kernel(wl))},
     }
     if bwd is not None:
         fb = useful_bwd_flops(wl)

@@ -155,12 +155,17 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
   if constexpr (MODE == DQ_CMP) { j_begin = 0; j_end = ((t_last + 1) / kBlock + kBlock - 1) / kBlock; }
   const int nblk = max(j_end - j_begin, 0);
 
+  // waves 0 .. LOADS / 4 - 1 copy four consecutive 1 KB pieces each (fewer
+  // waves spending scalar issue slots on the copies)
+  static_assert(LOADS % 4 == 0 && LOADS / 4 <= C::NW, "loader waves");
   auto issue = [&](int j, int bf) {
-    unsigned char* stage = ring + (size_t)bf * STAGE;
-    const unsigned char* src = img_b + (size_t)j * STAGE + 16 * l;
-    for (int pc = w; pc < LOADS; pc += C::NW)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024),
-                                       (void*)(stage + (size_t)pc * 1024), 16, 0, 0);
+    if (w < LOADS / 4) {
+      unsigned char* stage = ring + (size_t)bf * STAGE + (size_t)w * 4096;
+      const unsigned char* src = img_b + (size_t)j * STAGE + (size_t)w * 4096 + 16 * l;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+        __builtin_amdgcn_global_load_lds((const void*)(src + q2 * 1024), (void*)(stage + q2 * 1024), 16, 0, 0);
+    }
   };
 
   f32x4 acc[MT];

@@ -34,6 +34,26 @@ hipError_t launch_cmp_select(bool is_bf16, const Shape& s, const void* q, const 
 // K3: selection + window + gated combine.  knorm from K1 (required).
 //   lse / o_sel: selection branch log-sum-exp [B][Hq][T] and output (nullable);
 //   lse_win / o_win: the same for the window branch (nullable).
+// arguments of the selection / window kernels (K3)
+struct SelWinArgs {
+  const void* q;
+  const void* k;
+  const void* kvimg;   // [B][Hkv][nc] staged K / V^T images of the blocks (KvImage)
+  const void* gates;
+  const void* o_cmp;
+  const float* knorm;  // [B][Hkv][nc] largest key norm of each block
+  const int32_t* indices;
+  void* out;
+  float* lse;
+  void* o_sel;
+  float* lse_win;
+  void* o_win;
+};
+// K3 with packed selection items (sel_compact.hip): bf16, head_dim 64, four
+// query heads per KV group, window range within 32 blocks, LDS within 160 KB
+bool sel_compact_eligible(bool is_bf16, const Shape& s);
+hipError_t launch_sel_compact(const Shape& s, const SelWinArgs& args, hipStream_t st);
+
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
                           const void* kvimg, const void* gates, const void* o_cmp,
                           const float* knorm, const int32_t* indices, void* out, float* lse,

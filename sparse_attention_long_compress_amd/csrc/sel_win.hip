@@ -63,27 +63,16 @@
 #ifndef NSA_K3_FCH128
 #define NSA_K3_FCH128 2
 #endif
+// packed selection items for the shapes sel_compact.hip covers (0: general kernel)
+#ifndef NSA_K3_COMPACT
+#define NSA_K3_COMPACT 1
+#endif
 // LDS budget of the staging ring (bytes); the ring takes as many stages as fit
 #ifndef NSA_K3_RING_BYTES
 #define NSA_K3_RING_BYTES (144 * 1024)
 #endif
 
 namespace nsa {
-
-struct SelWinArgs {
-  const void* q;
-  const void* k;
-  const void* kvimg;   // [B][Hkv][nc] staged K / V^T images of the blocks (KvImage)
-  const void* gates;
-  const void* o_cmp;
-  const float* knorm;  // [B][Hkv][nc] largest key norm of each block
-  const int32_t* indices;
-  void* out;
-  float* lse;
-  void* o_sel;
-  float* lse_win;
-  void* o_win;
-};
 
 template <typename T, int D, int G>
 struct K3Cfg {
@@ -303,14 +292,19 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
   const int j_begin = need_sel ? 0 : j_win0;
   const int nblk = c_last - j_begin + 1;
 
-  // stage loads: this wave's 1 KB pieces (w, w + NW, ...) of block j's image
-  // into ring slot bf; lane l copies its 16 bytes of a piece
+  // stage loads of block j's image into ring slot bf; lane l copies its 16
+  // bytes of a piece
+  // waves 0 .. LOADS / 4 - 1 copy four consecutive 1 KB pieces each (fewer
+  // waves spending scalar issue slots on the copies)
+  static_assert(LOADS % 4 == 0 && LOADS / 4 <= C::NW, "loader waves");
   auto issue = [&](int j, int bf) {
-    unsigned char* stage = ring + (size_t)bf * STAGE;
-    const unsigned char* src = img_b + (size_t)j * STAGE + 16 * l;
-    for (int pc = w; pc < LOADS; pc += C::NW)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)pc * 1024),
-                                       (void*)(stage + (size_t)pc * 1024), 16, 0, 0);
+    if (w < LOADS / 4) {
+      unsigned char* stage = ring + (size_t)bf * STAGE + (size_t)w * 4096;
+      const unsigned char* src = img_b + (size_t)j * STAGE + (size_t)w * 4096 + 16 * l;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+        __builtin_amdgcn_global_load_lds((const void*)(src + q2 * 1024), (void*)(stage + q2 * 1024), 16, 0, 0);
+    }
   };
 
   float l_s[NCG], l_w[NCG];
@@ -557,6 +551,7 @@ hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const voi
                           const float* knorm, const int32_t* indices, void* out, float* lse,
                           void* o_sel, float* lse_win, void* o_win, hipStream_t st) {
   SelWinArgs a{q, k, kvimg, gates, o_cmp, knorm, indices, out, lse, o_sel, lse_win, o_win};
+  if (NSA_K3_COMPACT && sel_compact_eligible(is_bf16, s)) return launch_sel_compact(s, a, st);
   if (is_bf16) {
     if (s.D == 64) return launch_sw_g<bf16, 64>(s, a, st);
     return launch_sw_g<bf16, 128>(s, a, st);

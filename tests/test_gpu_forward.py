@@ -85,6 +85,11 @@ CASES = [
     ("1b3-gqa4", 512, 0.0, {"batch": 2, "top_k": 2, "window": 1}),
     ("340m-gqa4", 640, 1.0, {"top_k": 3, "window": 1000}),
     ("tiny-fp32", 256, 0.0, {"n_q_heads": 16, "n_kv_heads": 1}),
+    # four heads per group at head_dim 64 take the packed-selection kernel: three
+    # batch entries (12 KV groups, an ungrouped workgroup order) and a ragged tile
+    ("340m-gqa4", 1024, 1.0, {"batch": 3}),
+    # a window range beyond 32 blocks falls back to the general kernel
+    ("340m-gqa4", 2048, 1.0, {"window": 2048}),
 ]
 
 
