@@ -19,12 +19,12 @@
 //   Pass 2: recompute S^T, p = exp(s - lse), sum p over the G heads of each
 //           position with DPP (adjacent lanes), stage S[position][block] in LDS
 //           64 candidates at a time; each wave scans its share of them with
-//           one lane per position keeping a top-m list in registers, and the
-//           waves' lists are merged at the end.  A candidate is a 32-bit key: the score
-//           in fixed point (21 bits over [0, G], resolution G / 2^21) above the
-//           field 2047 - j, so "higher score, then lower index" is one unsigned
-//           compare and inserting into the sorted list is one v_med3_u32 per
-//           entry.
+//           one lane per position keeping a sorted top-m list in registers
+//           (each wave's candidates of a chunk are sorted by a bitonic network
+//           and merged in), and the waves' lists are merged pairwise at the
+//           end.  A candidate is a 32-bit key: the score in fixed point (21
+//           bits over [0, G], resolution G / 2^21) above the field 2047 - j,
+//           so "higher score, then lower index" is one unsigned compare.
 // For bf16 inputs the scores use the pooled keys as hi + lo (the rounded mean
 // plus its bf16 residual, two MFMAs), so rounding Kc to bf16 does not move the
 // importance by more than ~1e-6.
@@ -42,14 +42,41 @@ __device__ __forceinline__ uint32_t topk_key(float score, float qscale, int j) {
   const float f = fminf(fmaxf(score * qscale, 0.f), 2097151.f);
   return ((uint32_t)f << 11) | (kIdxMask - (uint32_t)j);
 }
-__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
-  return max(min(a, b), min(max(a, b), c));
-}
+// Top N of two descending lists a, b (N a power of two), into a: the pairwise
+// maxima of a and b reversed are the N largest of the union as a bitonic
+// sequence, which log2(N) compare-exchange stages sort descending.
 template <int N>
-__device__ __forceinline__ void insert_desc(uint32_t (&list)[N], uint32_t x) {
+__device__ __forceinline__ void merge_desc(uint32_t (&a)[N], const uint32_t (&b)[N]) {
 #pragma unroll
-  for (int i = N - 1; i >= 1; --i) list[i] = umed3(list[i], list[i - 1], x);
-  list[0] = max(list[0], x);
+  for (int i = 0; i < N; ++i) a[i] = max(a[i], b[N - 1 - i]);
+#pragma unroll
+  for (int d = N / 2; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & d) == 0) {
+        const uint32_t hi = max(a[i], a[i + d]), lo = min(a[i], a[i + d]);
+        a[i] = hi;
+        a[i + d] = lo;
+      }
+}
+
+// sort N keys descending (N a power of two; bitonic network of min / max)
+template <int N>
+__device__ __forceinline__ void sort_desc(uint32_t (&a)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int d = k / 2; d >= 1; d >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int p = i ^ d;
+        if (p > i) {
+          const bool desc = (i & k) == 0;
+          const uint32_t hi = max(a[i], a[p]), lo = min(a[i], a[p]);
+          a[i] = desc ? hi : lo;
+          a[p] = desc ? lo : hi;
+        }
+      }
 }
 
 template <typename T, int D, int G>
@@ -81,7 +108,7 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   __shared__ __align__(16) T Ls[64 * KST];
   __shared__ __align__(16) T Vs[D * VST];
   __shared__ float S_l[P][65];
-  __shared__ uint32_t mlist[NW - 1][P][LMAX];
+  __shared__ uint32_t mlist[(NW + 1) / 2][P][LMAX + 1];  // lists handed over in a merge round
 
   const int NTL = s.T / P;
   int bg, tile;
@@ -244,24 +271,37 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
         }
       }
       __syncthreads();
-      // wave w scans candidates jb + CPW w .. jb + CPW (w + 1) - 1, one lane per position
+      // wave w takes candidates jb + CPW w .. jb + CPW (w + 1) - 1, one lane per
+      // position: all read at once, sorted by a network, merged into the list
+      // (a missing candidate is key 0)
       if (l < P) {
         const int j0 = jb + CPW * w, j1 = min(jb + CPW * w + CPW, c);
-        for (int jj = j0; jj < j1; ++jj) insert_desc(list, topk_key(S_l[l][jj - jb], qscale, jj));
+        uint32_t cand[LMAX];
+#pragma unroll
+        for (int k = 0; k < LMAX; ++k)
+          cand[k] = (k < CPW && j0 + k < j1) ? topk_key(S_l[l][j0 + k - jb], qscale, j0 + k) : 0u;
+        static_assert(CPW <= LMAX && (CPW & (CPW - 1)) == 0, "candidates per wave");
+        uint32_t (&c8)[CPW] = *reinterpret_cast<uint32_t(*)[CPW]>(cand);
+        sort_desc(c8);
+        merge_desc(list, cand);
       }
     }
-    // merge the per-wave lists into wave 0's
-    __syncthreads();
-    if (w > 0 && l < P) {
+    // merge the per-wave lists pairwise into wave 0's: in the round of stride
+    // st, wave w + st hands its list to wave w (w a multiple of 2 st)
 #pragma unroll
-      for (int i = 0; i < LMAX; ++i) mlist[w - 1][l][i] = list[i];
-    }
-    __syncthreads();
-    if (w == 0 && l < P) {
-      // a rolled loop: fully unrolled chains of med3 insertions make the
-      // compiler's min/max combining blow up
-#pragma nounroll
-      for (int vi = 0; vi < (NW - 1) * LMAX; ++vi) insert_desc(list, mlist[vi / LMAX][l][vi % LMAX]);
+    for (int st = 1; st < NW; st <<= 1) {
+      __syncthreads();
+      if (w % (2 * st) == st && l < P) {
+#pragma unroll
+        for (int i = 0; i < LMAX; ++i) mlist[w / (2 * st)][l][i] = list[i];
+      }
+      __syncthreads();
+      if (w % (2 * st) == 0 && w + st < NW && l < P) {
+        uint32_t other[LMAX];
+#pragma unroll
+        for (int i = 0; i < LMAX; ++i) other[i] = mlist[w / (2 * st)][l][i];
+        merge_desc(list, other);
+      }
     }
   }
 
