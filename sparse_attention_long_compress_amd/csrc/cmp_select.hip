@@ -129,16 +129,21 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   const T* kcl_b = has_lo ? kcl + (size_t)b * s.nc * kc_row + (size_t)g * D : nullptr;
   const T* vct_b = vct + ((size_t)b * s.Hkv + g) * (size_t)D * s.ncp;
 
+  // 16-byte chunk c of pooled-key row r in LDS: rows 16..31 (mod 32) are
+  // rotated by four chunks so that the 16 rows one MFMA fragment read touches
+  // (r and r + 16 among them) fall in distinct bank groups
+  auto kchunk = [](int r, int c) { return c ^ (((r >> 4) & 1) << 2); };
   // stage pooled keys (and the residual) of blocks jb .. jb+63, and optionally
   // the pooled values; rows past the last complete block are clamped (masked)
   auto stage = [&](int jb, bool with_v) {
     for (int i = threadIdx.x; i < 64 * (D / EPV); i += NT) {
       const int r = i / (D / EPV), c8 = i % (D / EPV);
       const int key = min(jb + r, s.nc - 1);
-      *reinterpret_cast<int4*>(Ks + r * KST + c8 * EPV) =
+      const int cs = kchunk(r, c8);
+      *reinterpret_cast<int4*>(Ks + r * KST + cs * EPV) =
           *reinterpret_cast<const int4*>(kc_b + (size_t)key * kc_row + c8 * EPV);
       if (has_lo)
-        *reinterpret_cast<int4*>(Ls + r * KST + c8 * EPV) =
+        *reinterpret_cast<int4*>(Ls + r * KST + cs * EPV) =
             *reinterpret_cast<const int4*>(kcl_b + (size_t)key * kc_row + c8 * EPV);
     }
     if (with_v)
@@ -152,12 +157,14 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   auto scores = [&](int h, int u, const FragT (&qf)[KS]) -> f32x4 {
     const int kr = h * 32 + 8 * (col / 4) + 4 * u + (col % 4);
     f32x4 acc = zero4();
+    // elements ks * 32 + 8 a .. + 7 of the row: chunk (ks * 32 + 8 a) / EPV
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mma(acc, Frag<T>::load(Ks + kr * KST + ks * 32 + a * 8), qf[ks]);
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mma(acc, Frag<T>::load(Ks + kr * KST + kchunk(kr, (ks * 32 + a * 8) / EPV) * EPV), qf[ks]);
     if (has_lo) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        acc = mma(acc, Frag<T>::load(Ls + kr * KST + ks * 32 + a * 8), qf[ks]);
+        acc = mma(acc, Frag<T>::load(Ls + kr * KST + kchunk(kr, (ks * 32 + a * 8) / EPV) * EPV), qf[ks]);
     }
     return acc;
   };
