@@ -24,6 +24,9 @@ Parity-pin status (what pins each function; see tests/test_oracle_pins.py):
   forward/out       zero gates, unit gates, linearity, shift invariances
   select_bwd        central finite differences, torch autograd of causal and
                     masked SDPA
+  decode            the forward restricted to the last row of each prefix (its
+                    definition); pinned by an explicit per-query enumeration of
+                    the compressed, selected and window key sets in the tests
 """
 from __future__ import annotations
 
@@ -209,3 +212,38 @@ def backward(q, k, v, gates, indices, dout, *, top_k: int, window: int, blk: int
     if rc != 0:
         raise ValueError(f"nsa_oracle_backward failed: {rc}")
     return dq, dk, dv, dg
+
+
+def decode(q, k_cache, v_cache, gates, seq_lens, *, top_k: int, window: int, blk: int = 64,
+           scale: float | None = None, indices=None, threads: int | None = None):
+    """One decode step ("DeepSeek's Native Sparse Attention", How Does NSA Work?,
+    for a single query): sequence b of length L = seq_lens[b] has its query at
+    t = L - 1, and its output is the prefill output of row t over the first L
+    positions.  q [B,Hq,D], k_cache/v_cache [B,Lmax,Hkv,D], gates [B,Hq,3].
+    ``indices`` (optional int32 [B,Hkv,top_k]) freezes the selection.
+    Returns out, o_cmp, o_sel, o_win [B,Hq,D], indices [B,Hkv,top_k] and the
+    k-th vs (k+1)-th importance gap [B,Hkv]."""
+    q, kc, vc, gates = _f64(q), _f64(k_cache), _f64(v_cache), _f64(gates)
+    B, Hq, D = q.shape
+    Hkv = kc.shape[2]
+    res = {n: np.zeros((B, Hq, D)) for n in ("out", "o_cmp", "o_sel", "o_win")}
+    res["indices"] = np.zeros((B, Hkv, top_k), dtype=np.int32)
+    res["gap"] = np.zeros((B, Hkv))
+    for b in range(B):
+        L = int(seq_lens[b])
+        t = L - 1
+        qf = np.zeros((1, L, Hq, D))
+        qf[0, t] = q[b]
+        gf = np.zeros((1, L, Hq, 3))
+        gf[0, t] = gates[b]
+        idx = None
+        if indices is not None:
+            idx = np.zeros((1, Hkv, L, top_k), dtype=np.int32)
+            idx[0, :, t] = np.asarray(indices)[b]
+        r = forward(qf, kc[b:b + 1, :L], vc[b:b + 1, :L], gf, top_k=top_k, window=window,
+                    blk=blk, scale=scale, indices=idx, rows=[t], threads=threads)
+        for n in ("out", "o_cmp", "o_sel", "o_win"):
+            res[n][b] = r[n][0, t]
+        res["indices"][b] = r["indices"][0, :, t]
+        res["gap"][b] = r["gap"][0, :, t]
+    return res

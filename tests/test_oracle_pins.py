@@ -541,3 +541,83 @@ def test_backward_selection_part_equals_select_bwd():
     rq, rk, rv = oracle.select_bwd(q, k, v, g, idx, dout, top_k=topk)
     for a, b_ in ((dq, rq), (dk, rk), (dv, rv)):
         np.testing.assert_allclose(a, b_, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- decode step
+def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
+    """One query at t = L - 1 written out from the method's statement: mean of
+    each complete block, softmax over the blocks complete at t, importance
+    summed over the group's heads, blocks 0 and t // blk forced, the rest by
+    (importance desc, index asc), one softmax over the selected tokens s <= t,
+    one over t - W < s <= t, outputs mixed by the gates."""
+    Hq, D = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    tau = 1.0 / np.sqrt(D)
+    t = L - 1
+    own, nc = t // blk, L // blk
+    out = np.zeros((Hq, D))
+    chosen_all = []
+    for g in range(Hkv):
+        heads = range(g * G, (g + 1) * G)
+        Kc = [K[j * blk:(j + 1) * blk, g].mean(0) for j in range(nc)]
+        Vc = [V[j * blk:(j + 1) * blk, g].mean(0) for j in range(nc)]
+        p_cmp = {}
+        for h in heads:
+            if nc == 0:
+                p_cmp[h] = np.zeros(0)
+                continue
+            z = np.array([tau * q[h] @ Kc[j] for j in range(nc)])
+            e = np.exp(z - z.max())
+            p_cmp[h] = e / e.sum()
+        forced = [0] if own == 0 else [0, own]
+        cands = list(range(1, own))
+        m = top_k - len(forced)
+        if len(cands) <= m:
+            pick = cands
+        else:
+            imp = {j: sum(p_cmp[h][j] for h in heads) for j in cands}
+            pick = sorted(cands, key=lambda j: (-imp[j], j))[:m]
+        chosen = sorted(forced + pick)
+        chosen_all.append(chosen + [-1] * (top_k - len(chosen)))
+        sel_keys = [s for j in chosen for s in range(j * blk, (j + 1) * blk) if s <= t]
+        win_keys = list(range(max(0, t - W + 1), t + 1))
+        for h in heads:
+            def attend(keys):
+                z = np.array([tau * q[h] @ K[s, g] for s in keys])
+                e = np.exp(z - z.max())
+                return (e / e.sum()) @ np.array([V[s, g] for s in keys])
+            o_cmp = sum(p_cmp[h][j] * Vc[j] for j in range(nc)) if nc else np.zeros(D)
+            out[h] = gates[h, 0] * o_cmp + gates[h, 1] * attend(sel_keys) + gates[h, 2] * attend(win_keys)
+    return out, np.array(chosen_all)
+
+
+def test_decode_matches_per_query_enumeration():
+    rng = np.random.default_rng(7)
+    B, Lmax, Hq, Hkv, D, top_k, W = 7, 768, 4, 2, 8, 3, 40
+    lens = [1, 63, 64, 128, 150, 700, 768]
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((B, Lmax, Hkv, D))
+    vc = rng.standard_normal((B, Lmax, Hkv, D))
+    gates = rng.random((B, Hq, 3))
+    got = oracle.decode(q, kc, vc, gates, lens, top_k=top_k, window=W)
+    for b, L in enumerate(lens):
+        ref, idx = _decode_by_enumeration(q[b], kc[b, :L], vc[b, :L], gates[b], L, top_k, W)
+        np.testing.assert_allclose(got["out"][b], ref, atol=1e-12, rtol=1e-10)
+        assert np.array_equal(got["indices"][b], idx), (L, got["indices"][b], idx)
+
+
+def test_decode_is_independent_of_cache_past_the_length():
+    # positions >= L must not influence the step
+    rng = np.random.default_rng(8)
+    B, Lmax, Hq, Hkv, D = 2, 256, 4, 1, 8
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((B, Lmax, Hkv, D))
+    vc = rng.standard_normal((B, Lmax, Hkv, D))
+    gates = rng.random((B, Hq, 3))
+    a = oracle.decode(q, kc, vc, gates, [100, 200], top_k=3, window=30)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[0, 100:] = 1e3
+    vc2[1, 200:] = -1e3
+    b = oracle.decode(q, kc2, vc2, gates, [100, 200], top_k=3, window=30)
+    assert np.array_equal(a["out"], b["out"])
