@@ -236,6 +236,35 @@ nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const voi
                           void* dq, void* dk, void* dv, void* dgates, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/* One decode step: NSA for the newest position of each sequence over its KV
+ * cache ([DSA] How Does NSA Work?: the three branches and the gate mix,
+ * evaluated for a single query; [SIC] Method).  Sequence b has length
+ * L_b = seq_lens[b] and its newest key and value are already in the cache, so
+ * its query sits at t = L_b - 1 and the result is the prefill output row t of
+ * that prefix (compressed blocks j < L_b / 64, selection among 1 .. t/64 - 1
+ * plus blocks 0 and t/64, window t - W < s <= t).
+ *   q        : [B][Hq][D], the new queries.
+ *   k_cache, v_cache : [B][Lmax][Hkv][D]; positions >= L_b are never read.
+ *   k_cmp, v_cmp     : [B][Lmax/64][Hkv][D], the mean-pooled complete blocks
+ *              of the cache (nsa_pool of the cache, or kept up to date by the
+ *              caller as blocks complete); blocks >= L_b / 64 are never read.
+ *   seq_lens : int32 [B] on the device, 1 <= L_b <= Lmax; values outside are
+ *              clamped to that range (the kernel cannot report them).
+ *   gates    : [B][Hq][3] (g_cmp, g_sel, g_win).
+ *   params   : batch = B, seq_len = Lmax (the cache capacity, a multiple of
+ *              64), heads, head_dim, top_k, window, scale, dtype as for the
+ *              prefill; flags: NSA_SKIP_* only (NSA_INDICES_IN is
+ *              NSA_ERR_UNSUPPORTED).
+ *   out      : [B][Hq][D], overwritten.
+ *   indices  : optional int32 [B][Hkv][top_k]: the selected blocks,
+ *              ascending, -1 padded.
+ * No workspace; the kernel's on-chip memory grows with Lmax, the query heads
+ * per group and the window: NSA_ERR_UNSUPPORTED when it would exceed 160 KB. */
+nsa_status_t nsa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const void* k_cmp, const void* v_cmp, const int32_t* seq_lens,
+                        const void* gates, const nsa_params_t* p, void* out, int32_t* indices,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ SKIP_CMP_OUT, SKIP_SEL, SKIP_WIN, INDICES_IN = 1, 2, 4, 8
 EXPORTED = (
     "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_workspace_size",
     "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
-    "nsa_forward_train", "nsa_backward", "nsa_select_bwd_single",
+    "nsa_forward_train", "nsa_backward", "nsa_select_bwd_single", "nsa_decode",
 )
 
 
@@ -84,6 +84,8 @@ def lib():
         L.nsa_forward_train.argtypes = [vp, vp, vp, vp, P, vp, S, vp, ctypes.c_size_t, vp]
         L.nsa_forward_train.restype = ctypes.c_int
         L.nsa_backward.argtypes = [vp, vp, vp, vp, S, vp, P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.nsa_decode.restype = ctypes.c_int
+        L.nsa_decode.argtypes = [vp, vp, vp, vp, vp, i32p, vp, P, vp, i32p, vp]
         L.nsa_backward.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -305,3 +307,26 @@ def select_bwd_single(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, s
                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                                        _stream(stream)), "nsa_select_bwd_single")
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, k_cmp, v_cmp, seq_lens, gates, *, top_k, window, scale=None,
+           flags=0, want_indices=False, out=None, stream=None):
+    """One decode step (nsa_decode): q [B, Hq, D]; caches [B, Lmax, Hkv, D];
+    pooled caches [B, Lmax/64, Hkv, D]; seq_lens int32 [B] on the device; gates
+    [B, Hq, 3].  Returns {'out': [B, Hq, D]} (+ 'indices' [B, Hkv, top_k])."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    p = make_params(B, Lmax, Hq, Hkv, D, top_k=top_k, window=window, dtype=_dtype_code(q),
+                    scale=scale, flags=flags)
+    res = {"out": out if out is not None else torch.empty_like(q)}
+    idx = None
+    if want_indices:
+        idx = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
+        res["indices"] = idx
+    if seq_lens.dtype != torch.int32:
+        raise NsaError("seq_lens must be int32")
+    _check(lib().nsa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cmp), _ptr(v_cmp),
+                            _ptr(seq_lens), _ptr(gates), ctypes.byref(p), _ptr(res["out"]),
+                            _ptr(idx), _stream(stream)), "nsa_decode")
+    return res

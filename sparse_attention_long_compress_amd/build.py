@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnsa.so")
-SOURCES = ["api.hip", "pool.hip", "cmp_select.hip", "sel_win.hip", "sel_compact.hip", "bwd.hip", "bwd_dq.hip", "bwd_dkdv.hip", "bwd_single.hip"]
+SOURCES = ["api.hip", "pool.hip", "cmp_select.hip", "sel_win.hip", "sel_compact.hip", "bwd.hip", "bwd_dq.hip", "bwd_dkdv.hip", "bwd_single.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -415,3 +415,21 @@ nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const voi
 }
 
 }  // extern "C"
+
+nsa_status_t nsa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const void* k_cmp, const void* v_cmp, const int32_t* seq_lens,
+                        const void* gates, const nsa_params_t* p, void* out, int32_t* indices,
+                        void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (p->flags & NSA_INDICES_IN) return NSA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !k_cmp || !v_cmp || !seq_lens || !gates || !out) return NSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_cmp) ||
+      !aligned16(v_cmp) || !aligned16(gates) || !aligned16(out) || ((uintptr_t)seq_lens & 3u) ||
+      (indices && ((uintptr_t)indices & 3u)))
+    return NSA_ERR_ALIGN;
+  const Shape s = make_shape(p);
+  if (nsa::decode_lds_bytes(s) > 160 * 1024) return NSA_ERR_UNSUPPORTED;
+  return launched(nsa::launch_decode(p->dtype == NSA_BF16, s, q, k_cache, v_cache, k_cmp, v_cmp,
+                                     seq_lens, gates, out, indices, (hipStream_t)stream));
+}

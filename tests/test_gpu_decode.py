@@ -1,0 +1,136 @@
+"""Decode step (nsa_decode) against the oracle: one new query per sequence over
+a KV cache, sequences of different lengths in one batch.
+
+Cache positions at or past a sequence's length hold NaN on the device (and
+the pooled blocks built from them are NaN too): the step must never read them.
+Indices must match the oracle's wherever its importance gap exceeds 1e-3; the
+outputs are compared with the oracle run on the GPU's own selection (the same
+rule the prefill tests use for near-ties)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_long_compress_amd as nsa
+from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64
+from nsa_cases import GAP_TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def decode_inputs(wl, B, Lmax, lens, seed, planted_sigma=0.0):
+    """Seeded caches, queries and gates of the workload's shapes (q/k/v N(0,1),
+    gates sigmoid(N(0,1)); q and k rescaled to norm sqrt(D) for QK-norm
+    workloads; planted_sigma adds a per-block offset to the keys)."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    k = rng.standard_normal((B, Lmax, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Lmax, Hkv, D), dtype=np.float32)
+    gates = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, Hq, 3))))).astype(np.float32)
+    if wl.qk_norm:
+        for x in (q, k):
+            x *= (np.sqrt(D) / np.sqrt((x.astype(np.float64) ** 2).sum(-1, keepdims=True))).astype(np.float32)
+    if planted_sigma > 0:
+        off = rng.standard_normal((B, Lmax // 64, Hkv, D), dtype=np.float32) * np.float32(planted_sigma)
+        k += np.repeat(off, 64, axis=1)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    cpu = {n: torch.from_numpy(np.ascontiguousarray(a)).to(tdt) for n, a in
+           (("q", q), ("k", k), ("v", v), ("gates", gates))}
+    f64 = {n: as_f64(t) for n, t in cpu.items()}
+    dev = {n: t.to("cuda") for n, t in cpu.items()}
+    for b, L in enumerate(lens):  # what lies past the length must never be read
+        dev["k"][b, L:] = float("nan")
+        dev["v"][b, L:] = float("nan")
+    dev["kc"], dev["vc"] = nsa.pool(dev["k"], dev["v"])
+    dev["lens"] = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    return dev, f64
+
+
+def run_case(wl, B, Lmax, lens, seed=0, flags=0, planted_sigma=0.0):
+    _print("case", wl.name, wl.head_dim, wl.n_q_heads, wl.n_kv_heads, wl.dtype, B, Lmax, lens, flags)
+    dev, f64 = decode_inputs(wl, B, Lmax, lens, seed, planted_sigma)
+    res = nsa.decode(dev["q"], dev["k"], dev["v"], dev["kc"], dev["vc"], dev["lens"], dev["gates"],
+                     top_k=wl.top_k, window=wl.window, scale=wl.scale, flags=flags,
+                     want_indices=True)
+    torch.cuda.synchronize()
+    gates = f64["gates"].copy()
+    if flags & nsa.SKIP_CMP_OUT:
+        gates[..., 0] = 0
+    if flags & nsa.SKIP_SEL:
+        gates[..., 1] = 0
+    if flags & nsa.SKIP_WIN:
+        gates[..., 2] = 0
+    ora = oracle.decode(f64["q"], f64["k"], f64["v"], gates, lens, top_k=wl.top_k,
+                        window=wl.window, scale=wl.scale)
+    gi = res["indices"].cpu().numpy()
+    decisive = ora["gap"] > GAP_TOL
+    agree = np.all(gi == ora["indices"], axis=-1)
+    assert np.all(agree[decisive]), "indices differ on decisive (sequence, group) pairs"
+    _print("index agreement", agree.mean(), "decisive", decisive.mean())
+    # outputs against the oracle with the GPU's selection (near-ties may differ)
+    ora2 = oracle.decode(f64["q"], f64["k"], f64["v"], gates, lens, top_k=wl.top_k,
+                         window=wl.window, scale=wl.scale, indices=gi)
+    got = res["out"].double().cpu().numpy()
+    assert_close(got, ora2["out"], wl.dtype, "decode out")
+    return agree, decisive
+
+
+W340 = WORKLOADS["340m-gqa4"]
+W13 = WORKLOADS["1b3-gqa4"]
+WMQA = WORKLOADS["mqa-ablation"]
+WTINY = WORKLOADS["tiny-fp32"]
+
+CASES = [
+    # workload, B, Lmax, lengths
+    (W340, 6, 4096, [1, 63, 64, 700, 2048, 4096]),
+    (W340.with_(top_k=3, window=100), 4, 1024, [65, 130, 640, 1024]),
+    (W340.with_(window=5000), 3, 2048, [5, 1000, 2048]),          # window covers the prefix
+    (W340.with_(top_k=32), 2, 1024, [700, 1024]),                 # k covers every block
+    (W340.with_(n_q_heads=4, n_kv_heads=4), 3, 1024, [64, 500, 1000]),   # G = 1
+    (W340.with_(n_q_heads=8, n_kv_heads=4), 3, 1024, [64, 500, 1000]),   # G = 2
+    (W13, 3, 2048, [100, 1024, 2048]),
+    (W13.with_(n_q_heads=16, n_kv_heads=2), 2, 2048, [900, 2048]),       # G = 8
+    (WMQA, 2, 2048, [512, 1500]),                                        # G = 16
+    (WTINY, 3, 1024, [10, 300, 1024]),                                   # fp32
+]
+
+
+@pytest.mark.parametrize("wl,B,Lmax,lens", CASES, ids=[f"{c[0].name}-{i}" for i, c in enumerate(CASES)])
+def test_decode_matches_oracle(wl, B, Lmax, lens):
+    run_case(wl, B, Lmax, lens, seed=11)
+
+
+def test_decode_planted_selection_is_exact():
+    # planted block offsets make most selections decisive, so the exact-index
+    # rule covers most (sequence, group) pairs
+    _, decisive = run_case(W340, 4, 4096, [300, 1200, 3000, 4096], seed=12, planted_sigma=1.0)
+    assert decisive.mean() >= 0.75
+
+
+@pytest.mark.parametrize("flags", [nsa.SKIP_WIN, nsa.SKIP_CMP_OUT, nsa.SKIP_SEL,
+                                   nsa.SKIP_SEL | nsa.SKIP_CMP_OUT])
+def test_decode_skip_flags_equal_zero_gates(flags):
+    run_case(W340, 3, 2048, [200, 1500, 2048], seed=13, flags=flags)
+
+
+def test_decode_full_cache_size():
+    # the 340M shape at its full 8192-position capacity, 16 sequences
+    rng = np.random.default_rng(14)
+    lens = sorted(int(x) for x in rng.integers(1, 8193, 16))
+    lens[-1] = 8192
+    run_case(W340, 16, 8192, lens, seed=14)
+
+
+def test_decode_rejects_index_input():
+    wl = W340
+    dev, _ = decode_inputs(wl, 1, 128, [100], 0)
+    with pytest.raises(nsa.NsaError, match="UNSUPPORTED"):
+        nsa.decode(dev["q"], dev["k"], dev["v"], dev["kc"], dev["vc"], dev["lens"], dev["gates"],
+                   top_k=wl.top_k, window=wl.window, flags=nsa.INDICES_IN)
