@@ -203,6 +203,59 @@ def copy_calibration(nbytes):
     torch.cuda.synchronize()
 
 
+def decode_bench(nsa, torch, np, wl, steps, warmup, batch=64):
+    """One decode step (nsa_decode) for `batch` sequences of the workload's
+    shape at full cache length (the workload's seq_len), timed with HIP events
+    on the current stream.  Algorithmic HBM bytes per step: for every
+    (sequence, KV group) the K and V rows of the union of its selected blocks
+    and its window (keys <= t), its pooled keys and values, plus q, gates and
+    out; taken from the step's own selection."""
+    Lmax = wl.seq_len
+    Hq, Hkv, D = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed + 7)
+    k = torch.randn((batch, Lmax, Hkv, D), dtype=tdt, device="cuda", generator=gen)
+    v = torch.randn((batch, Lmax, Hkv, D), dtype=tdt, device="cuda", generator=gen)
+    q = torch.randn((batch, Hq, D), dtype=tdt, device="cuda", generator=gen)
+    gates = torch.sigmoid(torch.randn((batch, Hq, 3), device="cuda", generator=gen)).to(tdt)
+    kc, vc = nsa.pool(k, v)
+    lens = torch.full((batch,), Lmax, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    res = nsa.decode(q, k, v, kc, vc, lens, gates, top_k=wl.top_k, window=wl.window,
+                     scale=wl.scale, want_indices=True)
+    idx = res["indices"].cpu().numpy()
+    t = Lmax - 1
+    own, nc = t // 64, Lmax // 64
+    jw_lo = max(0, t - wl.window + 1) // 64
+    es = 2 if wl.dtype == "bf16" else 4
+    blocks = 0
+    for b in range(batch):
+        for g in range(Hkv):
+            sel = {int(j) for j in idx[b, g] if j >= 0}
+            blocks += len(sel | set(range(jw_lo, own + 1)))
+    nbytes = (blocks * 64 * D * 2 * es + batch * Hkv * nc * D * 2 * es
+              + batch * Hq * (2 * D + 3) * es)
+    for _ in range(warmup):
+        nsa.decode(q, k, v, kc, vc, lens, gates, top_k=wl.top_k, window=wl.window,
+                   scale=wl.scale, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        nsa.decode(q, k, v, kc, vc, lens, gates, top_k=wl.top_k, window=wl.window,
+                   scale=wl.scale, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    dt = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e-3
+    gbs = nbytes / dt / 1e9
+    return {"kernel": "decode_kernel", "batch": batch, "cache_len": Lmax,
+            "step_us": round(dt * 1e6, 2), "tokens_per_s": round(batch / dt, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": int(nbytes)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +275,9 @@ def main():
     ap.add_argument("--ab-single", action="store_true",
                     help="only time the two-pass selection backward against the single-pass one "
                          "with atomics (nsa_select_bwd_single) and print one JSON line")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave out the decode-step measurement (nsa_decode, 64 sequences at "
+                         "full cache length)")
     ap.add_argument("--no-backward", action="store_true",
                     help="time the forward only (the selection-branch backward and a training "
                          "step -- forward with saved tensors plus the full backward -- are timed "
@@ -369,7 +425,9 @@ def main():
     fl = useful_flops(wl)
     tokens = wl.batch * wl.seq_len
     if args.profile_only:
+        dec = None if args.no_decode else decode_bench(nsa, torch, np, wl, args.steps, args.warmup)
         print(json.dumps({"profile_only": True, "ms_per_step": wall * 1e3,
+                          "decode_us": None if dec is None else dec["step_us"],
                           "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6,
                           "sel_bwd_us": None if bwd is None else bwd * 1e6,
                           "train_fwd_us": None if train is None else train[0] * 1e6,
@@ -418,6 +476,8 @@ def main():
             "full_backward_useful_tflops": round(fbf / train[1] / 1e12, 2),
             "step_ms": round(step_s * 1e3, 4), "tokens_per_s": round(tokens / step_s, 1),
             "pct_bf16_peak": round(100 * (ff + fbf) / step_s / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_decode:
+        res["decode"] = decode_bench(nsa, torch, np, wl, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         f64 = {k: as_f64(v) for k, v in cpu.items()}
         res["cpu_baseline"] = cpu_baseline(wl, f64)

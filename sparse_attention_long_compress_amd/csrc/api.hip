@@ -429,7 +429,7 @@ nsa_status_t nsa_decode(const void* q, const void* k_cache, const void* v_cache,
       (indices && ((uintptr_t)indices & 3u)))
     return NSA_ERR_ALIGN;
   const Shape s = make_shape(p);
-  if (nsa::decode_lds_bytes(s) > 160 * 1024) return NSA_ERR_UNSUPPORTED;
+  if (nsa::decode_lds_bytes(p->dtype == NSA_BF16, s) > 160 * 1024) return NSA_ERR_UNSUPPORTED;
   return launched(nsa::launch_decode(p->dtype == NSA_BF16, s, q, k_cache, v_cache, k_cmp, v_cmp,
                                      seq_lens, gates, out, indices, (hipStream_t)stream));
 }

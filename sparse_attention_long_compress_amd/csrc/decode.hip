@@ -35,15 +35,21 @@
 namespace nsa {
 
 namespace {
-constexpr int kDecNW = 4;
-constexpr int kDecNT = kDecNW * kWave;
+// waves per workgroup: 8 for bf16 at head_dim 64, 4 otherwise (each wave
+// stages one 64-key V tile in LDS)
+template <typename T, int D>
+struct DecCfg {
+  static constexpr int NW = (sizeof(T) == 2 && D == 64) ? 8 : 4;
+  static constexpr int NT = NW * kWave;
+};
 
 struct DecLds {
   // float offsets into the dynamic LDS block
-  int qs, sc, imp, lse, pb, mrg, ml, ints, total_floats;
+  int qs, sc, imp, lse, vb, mrg, ml, ints, total_floats;
 };
 
-__host__ __device__ inline DecLds dec_lds(int G, int D, int ncap, int topk, int wmax_blocks) {
+__host__ __device__ inline DecLds dec_lds(int G, int D, int es, int NW, int ncap, int topk,
+                                          int wmax_blocks) {
   DecLds o;
   o.qs = 0;
   const int r0 = G * D;
@@ -51,12 +57,12 @@ __host__ __device__ inline DecLds dec_lds(int G, int D, int ncap, int topk, int 
   o.sc = r0;
   o.imp = r0 + G * ncap;
   const int endA = o.imp + ncap;
-  // phase B (same region): per-wave probabilities [NW][64][2G], per-wave
+  // phase B (same region): per-wave V tiles [NW][64][D] (input type), per-wave
   // partial outputs [NW][2][G][D] and their (max, sum) [NW][2][G][2]
-  o.pb = r0;
-  o.mrg = o.pb + kDecNW * 64 * 2 * G;
-  o.ml = o.mrg + kDecNW * 2 * G * D;
-  const int endB = o.ml + kDecNW * 2 * G * 2;
+  o.vb = r0;
+  o.mrg = o.vb + NW * 64 * D * es / 4;
+  o.ml = o.mrg + NW * 2 * G * D;
+  const int endB = o.ml + NW * 2 * G * 2;
   o.lse = (endA > endB ? endA : endB);
   o.ints = o.lse + G;
   // ints: selected blocks [32], count, walk list [topk + wmax_blocks], its
@@ -94,8 +100,9 @@ struct DecodeArgs {
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
-  constexpr int NT = kDecNT, NW = kDecNW;
+__global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, DecodeArgs a) {
+  constexpr int NT = DecCfg<T, D>::NT, NW = DecCfg<T, D>::NW;
+  typedef typename Frag<T>::type FragT;
   constexpr int CPL = D / kWave;  // channels per lane in P V
   const float NINF = -__builtin_inff();
   const int bg = blockIdx.x;
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
   const int topk = s.topk, W = s.W;
   const int jw_lo = win_on ? max(0, t - W + 1) / kBlock : own + 1;
   const int wmax_blocks = (W - 1) / kBlock + 2 < ncap ? (W - 1) / kBlock + 2 : ncap;
-  const DecLds lay = dec_lds(G, D, ncap, topk, wmax_blocks);
+  const DecLds lay = dec_lds(G, D, (int)sizeof(T), NW, ncap, topk, wmax_blocks);
 
   extern __shared__ __align__(16) float sm[];
   float* qs = sm + lay.qs;
@@ -197,6 +204,7 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
         if (e < G * D) {
           const int h = e / D, d = e % D;
           float acc = 0.f;
+#pragma unroll 8
           for (int j = 0; j < nc; ++j) acc += sc[h * ncap + j] * to_f32(vp[(size_t)j * row + d]);
           ocmp[i] = acc;
         }
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
   __syncthreads();
 
   // ---- 5. selection and window attention; wave w takes blocks w, w + NW, ...
-  float* pb = sm + lay.pb + w * 64 * 2 * G;  // this wave's probabilities [64][2G]
+  T* vb = reinterpret_cast<T*>(sm + lay.vb) + (size_t)w * 64 * D;  // this wave's V tile [64][D]
   float ms[G], ls[G], mw[G], lw[G];
   float os[G][CPL], ow[G][CPL];
 #pragma unroll
@@ -298,6 +306,12 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
     const bool valid = key <= t;
     const bool ins = is_sel && valid;
     const bool inw = win_on && valid && key > t - W;
+    // the V row of this lane's key: its 16-byte loads issued first, in
+    // flight during Q K
+    FragT vr[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i)
+      vr[i] = valid ? Frag<T>::load(vc + (size_t)key * row + 8 * i) : Frag<T>::zero();
     float x[G];
     if (valid) {
       qk(kc + (size_t)key * row, x);
@@ -305,12 +319,17 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) x[h] = 0.f;
     }
+    // the V row into row l of the wave's tile (zeros past t)
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) *reinterpret_cast<FragT*>(vb + l * D + 8 * i) = vr[i];
     const bool any_s = __builtin_amdgcn_ballot_w64(ins) != 0;
     const bool any_w = __builtin_amdgcn_ballot_w64(inw) != 0;
+    float ps[G], pw[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float xv = x[h] * c1;
-      float ps = 0.f, pw = 0.f;
+      ps[h] = 0.f;
+      pw[h] = 0.f;
       if (any_s) {
         const float bm = wave_max(ins ? xv : NINF);
         const float mn = fmaxf(ms[h], bm);
@@ -319,8 +338,8 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) os[h][c] *= al;
         ms[h] = mn;
-        ps = ins ? fast_exp2(xv - mn) : 0.f;
-        ls[h] += wave_sum(ps);
+        ps[h] = ins ? fast_exp2(xv - mn) : 0.f;
+        ls[h] += wave_sum(ps[h]);
       }
       if (any_w) {
         const float bm = wave_max(inw ? xv : NINF);
@@ -330,31 +349,37 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) ow[h][c] *= al;
         mw[h] = mn;
-        pw = inw ? fast_exp2(xv - mn) : 0.f;
-        lw[h] += wave_sum(pw);
+        pw[h] = inw ? fast_exp2(xv - mn) : 0.f;
+        lw[h] += wave_sum(pw[h]);
       }
-      pb[l * 2 * G + h] = ps;
-      pb[l * 2 * G + G + h] = pw;
     }
-    // P V: lane l now owns channels l, l + 64, ...; keys past t are not read
+    // P V: lane l now owns channels l, l + 64, ...; a key's probabilities come
+    // from its lane by readlane, its V row from the tile
     const int nk = min(kBlock, t - j * kBlock + 1);
-    const T* vrow = vc + (size_t)j * kBlock * row;
+#pragma unroll 4
     for (int kk = 0; kk < nk; ++kk) {
       float vv[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) vv[c] = to_f32(vrow[(size_t)kk * row + l + c * kWave]);
+      for (int c = 0; c < CPL; ++c) vv[c] = to_f32(vb[kk * D + l + c * kWave]);
+      if (any_s) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p1 = pb[kk * 2 * G + h], p2 = pb[kk * 2 * G + G + h];
+        for (int h = 0; h < G; ++h) {
+          const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps[h]), kk));
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          os[h][c] += p1 * vv[c];
-          ow[h][c] += p2 * vv[c];
+          for (int c = 0; c < CPL; ++c) os[h][c] += p1 * vv[c];
+        }
+      }
+      if (any_w) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pw[h]), kk));
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) ow[h][c] += p2 * vv[c];
         }
       }
     }
   }
-  __syncthreads();  // all waves past their last use of pb (the region is reused)
+  __syncthreads();  // all waves past their last use of the V tiles
 
   // ---- 6. combine the waves, gate, write
   float* mrg = sm + lay.mrg;  // [NW][2][G][D]
@@ -403,21 +428,23 @@ __global__ __launch_bounds__(kDecNT) void decode_kernel(Shape s, DecodeArgs a) {
   }
 }
 
-size_t decode_lds_bytes(const Shape& s) {
+size_t decode_lds_bytes(bool is_bf16, const Shape& s) {
   const int ncap = s.T / kBlock;
   const int wmax = (s.W - 1) / kBlock + 2 < ncap ? (s.W - 1) / kBlock + 2 : ncap;
-  return (size_t)dec_lds(s.G, s.D, ncap, s.topk, wmax).total_floats * 4;
+  const int es = is_bf16 ? 2 : 4;
+  const int NW = (is_bf16 && s.D == 64) ? DecCfg<bf16, 64>::NW : DecCfg<float, 64>::NW;
+  return (size_t)dec_lds(s.G, s.D, es, NW, ncap, s.topk, wmax).total_floats * 4;
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_dec(const Shape& s, const DecodeArgs& a, hipStream_t st) {
-  const size_t lds = decode_lds_bytes(s);
+  const size_t lds = decode_lds_bytes(sizeof(T) == 2, s);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<T, D, G>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(s.B * s.Hkv), dim3(kDecNT), lds, st, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(s.B * s.Hkv), dim3(DecCfg<T, D>::NT), lds, st, s, a);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ bool sel_compact_eligible(bool is_bf16, const Shape& s);
 hipError_t launch_sel_compact(const Shape& s, const SelWinArgs& args, hipStream_t st);
 
 // decode.hip: one new query per sequence over a KV cache
-size_t decode_lds_bytes(const Shape& s);
+size_t decode_lds_bytes(bool is_bf16, const Shape& s);
 hipError_t launch_decode(bool is_bf16, const Shape& s, const void* q, const void* kcache,
                          const void* vcache, const void* kcmp, const void* vcmp,
                          const int32_t* lens, const void* gates, void* out, int32_t* indices,
