@@ -71,19 +71,68 @@ __host__ __device__ inline DecLds dec_lds(int G, int D, int es, int NW, int ncap
   return o;
 }
 
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
-  const unsigned lo = __shfl_xor((unsigned)v, m), hi = __shfl_xor((unsigned)(v >> 32), m);
-  return ((unsigned long long)hi << 32) | lo;
+// Wave-wide reductions with in-register lane exchanges: DPP within each
+// 16-lane row (quad swaps, half-row and row mirrors), then the gfx950
+// permlane16 / permlane32 swaps across rows; no LDS crossbar round trips.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  auto dpp = [](float x, int ctrl) -> float {
+    switch (ctrl) {
+      case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+      case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+      case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
+    }
+  };
+  v = op(v, dpp(v, 0xB1));   // lane ^ 1
+  v = op(v, dpp(v, 0x4E));   // lane ^ 2
+  v = op(v, dpp(v, 0x141));  // the other quad of 8
+  v = op(v, dpp(v, 0x140));  // the other half of 16
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
+}
+// largest 64-bit key of the wave (the same exchanges on both halves)
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  auto mx = [](unsigned long long x, unsigned long long y) { return x > y ? x : y; };
+  auto dpp64 = [](unsigned long long x, int ctrl) -> unsigned long long {
+    int lo = (int)(unsigned)x, hi = (int)(unsigned)(x >> 32);
+    switch (ctrl) {
+      case 0xB1: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, true); break;
+      case 0x4E: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, true); break;
+      case 0x141: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, true); break;
+      default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, true); break;
+    }
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+  };
+  v = mx(v, dpp64(v, 0xB1));
+  v = mx(v, dpp64(v, 0x4E));
+  v = mx(v, dpp64(v, 0x141));
+  v = mx(v, dpp64(v, 0x140));
+  auto swap = [](unsigned long long x, bool p32) -> unsigned long long {
+    const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
+    if (p32) {
+      auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      const unsigned long long u = ((unsigned long long)b[0] << 32) | a[0];
+      const unsigned long long w = ((unsigned long long)b[1] << 32) | a[1];
+      return u > w ? u : w;
+    }
+    auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const unsigned long long u = ((unsigned long long)b[0] << 32) | a[0];
+    const unsigned long long w = ((unsigned long long)b[1] << 32) | a[1];
+    return u > w ? u : w;
+  };
+  v = swap(v, false);
+  return swap(v, true);
 }
 }  // namespace
 
@@ -240,11 +289,7 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
           unsigned long long best = 0ull;
 #pragma unroll
           for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) {
-            const unsigned long long other = shfl_xor_u64(best, o);
-            best = other > best ? other : best;
-          }
+          best = wave_max_u64(best);
 #pragma unroll
           for (int i = 0; i < PER; ++i)
             if (key[i] == best) key[i] = 0ull;  // keys are unique (the index field)
