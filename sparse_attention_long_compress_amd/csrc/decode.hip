@@ -253,7 +253,7 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
         if (e < G * D) {
           const int h = e / D, d = e % D;
           float acc = 0.f;
-#pragma unroll 8
+#pragma unroll 32
           for (int j = 0; j < nc; ++j) acc += sc[h * ncap + j] * to_f32(vp[(size_t)j * row + d]);
           ocmp[i] = acc;
         }
