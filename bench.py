@@ -48,9 +48,16 @@ def useful_counts(wl):
     return sel, win, cmp
 
 
-def useful_flops(wl):
+def useful_flops(wl, branches="all"):
+    """Useful forward FLOPs: 4 D per (query, head, attended key).  With the
+    compression output pruned only its scores (Q Kc^T, 2 D per pooled key) are
+    still needed for the selection; window-only needs the window alone."""
     sel, win, cmp = useful_counts(wl)
     per = 4 * wl.head_dim * wl.batch * wl.n_q_heads
+    if branches == "window":
+        sel, cmp = 0, 0
+    elif branches == "no-cmp":
+        cmp = cmp / 2
     return {"sel_win": per * (sel + win), "cmp": per * cmp, "total": per * (sel + win + cmp)}
 
 
@@ -275,6 +282,10 @@ def main():
     ap.add_argument("--ab-single", action="store_true",
                     help="only time the two-pass selection backward against the single-pass one "
                          "with atomics (nsa_select_bwd_single) and print one JSON line")
+    ap.add_argument("--branches", choices=("all", "no-cmp", "window"), default="all",
+                    help="branches in the output: all; no-cmp (compression output pruned, its scores "
+                         "still drive the selection); window (sliding window only) -- the pruned-branch "
+                         "layers of the MQA ablation.  Other than 'all' implies --no-backward --no-decode")
     ap.add_argument("--no-decode", action="store_true",
                     help="leave out the decode-step measurement (nsa_decode, 64 sequences at "
                          "full cache length)")
@@ -304,6 +315,10 @@ def main():
     from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64, draw, to_dtype
 
     wl = WORKLOADS[args.workload]
+    if args.branches != "all":
+        args.no_backward = True
+        args.no_decode = True
+    bflags = {"all": 0, "no-cmp": nsa.SKIP_CMP_OUT, "window": nsa.SKIP_CMP_OUT | nsa.SKIP_SEL}[args.branches]
     arrs = draw(wl, with_dout=not args.no_backward)
     cpu = to_dtype(arrs, wl.dtype)
     dev = {k: v.to("cuda") for k, v in cpu.items()}
@@ -341,7 +356,8 @@ def main():
 
     def step(events=None):
         nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
-                    window=wl.window, scale=wl.scale, out=out, workspace=ws, events=events)
+                    window=wl.window, scale=wl.scale, out=out, workspace=ws, events=events,
+                    flags=bflags)
 
     for _ in range(args.warmup):
         step()
@@ -422,7 +438,7 @@ def main():
     k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
     k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
     ev_step = np.mean([r[0].elapsed_time(r[3]) for r in evs]) * 1e-3
-    fl = useful_flops(wl)
+    fl = useful_flops(wl, args.branches)
     tokens = wl.batch * wl.seq_len
     if args.profile_only:
         dec = None if args.no_decode else decode_bench(nsa, torch, np, wl, args.steps, args.warmup)
@@ -451,7 +467,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "block": 64, "top_k": wl.top_k,
-                   "window": wl.window, "parallelism": "none (1 GPU)"},
+                   "window": wl.window, "branches": args.branches, "parallelism": "none (1 GPU)"},
         "useful_tflops": round(fl["total"] / wall / 1e12, 2),
         "pct_bf16_peak": round(100 * fl["total"] / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "stage_us": {"pool": round(k1 * 1e6, 2), "cmp_select": round(k2 * 1e6, 2),
