@@ -89,12 +89,15 @@ struct K2Cfg {
   static constexpr int CGW = RWV / 16;                       // column groups per wave
   static constexpr int CPW = 64 / NW;                        // top-k candidates per wave and chunk
   static constexpr int KS = D / 32, MT = D / 16;
+  // minimum waves per SIMD (launch bound): 4 at head_dim 64 -- two 8-wave
+  // workgroups per CU, at most 128 VGPRs; at 128 the registers allow one
+  static constexpr int MIN_WAVES_EU = (D == 64 && NW == 8) ? 4 : 1;
   static constexpr int KST = D + 8;   // LDS row stride of the pooled-key chunk
   static constexpr int VST = 64 + 8;  // LDS row stride of the pooled-value chunk
 };
 
 template <typename T, int D, int G, int LMAX>
-__global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
+__global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU)) void cmp_select_kernel(
     Shape s, const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ kcl,
     const T* __restrict__ vct, T* __restrict__ o_cmp, float* __restrict__ lse_cmp,
     int32_t* __restrict__ indices, int do_topk) {
@@ -104,11 +107,17 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT)) void cmp_select_kernel(
   typedef typename Frag<T>::type FragT;
   constexpr int EPV = 16 / sizeof(T);
 
-  __shared__ __align__(16) T Ks[64 * KST];
-  __shared__ __align__(16) T Ls[64 * KST];
+  // the pooled-key tiles (and their residuals) share storage with the lists
+  // the waves hand over when merging their top-k lists, which happens after
+  // the last chunk (keeps head_dim 128 at two workgroups per CU)
+  constexpr size_t KL_BYTES = 2 * 64 * KST * sizeof(T);
+  constexpr size_t ML_BYTES = (size_t)((NW + 1) / 2) * P * (LMAX + 1) * 4;
+  __shared__ __align__(16) unsigned char kl_raw[KL_BYTES > ML_BYTES ? KL_BYTES : ML_BYTES];
+  T* Ks = reinterpret_cast<T*>(kl_raw);
+  T* Ls = Ks + 64 * KST;
+  auto mlist = reinterpret_cast<uint32_t(*)[P][LMAX + 1]>(kl_raw);  // [(NW + 1) / 2][P][LMAX + 1]
   __shared__ __align__(16) T Vs[D * VST];
   __shared__ float S_l[P][65];
-  __shared__ uint32_t mlist[(NW + 1) / 2][P][LMAX + 1];  // lists handed over in a merge round
 
   const int NTL = s.T / P;
   int bg, tile;
