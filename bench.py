@@ -256,7 +256,8 @@ def decode_bench(nsa, torch, np, wl, steps, warmup, batch=64):
     torch.cuda.synchronize()
     dt = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e-3
     gbs = nbytes / dt / 1e9
-    return {"kernel": "decode_kernel", "batch": batch, "cache_len": Lmax,
+    return {"kernel": "decode_mfma_kernel" if wl.dtype == "bf16" else "decode_kernel",
+            "batch": batch, "cache_len": Lmax,
             "step_us": round(dt * 1e6, 2), "tokens_per_s": round(batch / dt, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -11,13 +11,13 @@
 // compressed probabilities (selection, ties to the lower index), and the keys
 // t - W < s <= t (window).
 //
-// One workgroup (4 waves) per (sequence b, KV group g), G query heads:
+// fp32 caches: one workgroup (4 waves) per (sequence b, KV group g), G query
+// heads (the bf16 kernel further below does the same on MFMA tiles):
 //   1. Q of the G heads into LDS (fp32);
 //   2. compressed scores, one pooled key per thread; per-head log-sum-exp;
 //      probabilities; o_cmp per (head, channel); importance per block;
-//   3. top-k by wave 0: 64-bit keys (fp32 importance bits above the inverted
-//      block index: one unsigned compare orders by score, then lower index),
-//      iterated wave maxima;
+//   3. top-k by wave 0 (topk_wave: radix select over unique keys made of the
+//      importance bits and the inverted block index);
 //   4. the blocks to read: the selected ones below the window, then the
 //      window's blocks; the waves take them round-robin.  Per block a lane
 //      owns a key for Q K (G dot products against Q in LDS), each branch keeps
@@ -48,6 +48,8 @@ struct DecLds {
   int qs, sc, imp, lse, vb, mrg, ml, ints, total_floats;
 };
 
+__host__ __device__ inline int al4(int x) { return (x + 3) & ~3; }  // 16-byte multiple
+
 __host__ __device__ inline DecLds dec_lds(int G, int D, int es, int NW, int ncap, int topk,
                                           int wmax_blocks) {
   DecLds o;
@@ -55,7 +57,7 @@ __host__ __device__ inline DecLds dec_lds(int G, int D, int es, int NW, int ncap
   const int r0 = G * D;
   // phase A: scores / probabilities [G][ncap] and importance [ncap]
   o.sc = r0;
-  o.imp = r0 + G * ncap;
+  o.imp = al4(r0 + G * ncap);  // 16-byte aligned: the top-k reads it four at a time
   const int endA = o.imp + ncap;
   // phase B (same region): per-wave V tiles [NW][64][D] (input type), per-wave
   // partial outputs [NW][2][G][D] and their (max, sum) [NW][2][G][2]
@@ -133,6 +135,71 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   };
   v = swap(v, false);
   return swap(v, true);
+}
+
+// Top-k of one (sequence, group), run by one wave (lane l): the forced blocks
+// 0 and own, then the m_free largest importances among blocks 1 .. own-1
+// (ties to the lower index), or every candidate when there are no more than
+// m_free.  selv[] receives the blocks in ascending order and *nsel their
+// count.
+//
+// Candidate j gets the key (fp32 importance bits << 10) | (1023 - j): keys
+// are unique, a larger key is a higher importance or an equal one at a lower
+// index (the importances are sums of exponentials, never negative, so their
+// bit patterns order like their values), and every candidate's key is >= 1.
+// The m_free-th largest key is found bit by bit from the top (radix select:
+// keep a bit when at least m_free keys reach the prefix with it set), with
+// one 64-bit compare and a ballot count per key slot and bit; the chosen
+// candidates are the keys at or above it, placed in ascending block order by
+// ballot prefix counts.
+__device__ void topk_wave(const float* imp, int own, int topk, bool need_topk, int l, int* selv,
+                          int* nsel) {
+  const int ncand = max(own - 1, 0);              // candidates 1 .. own-1
+  const int m_free = topk - (own == 0 ? 1 : 2);
+  if (!need_topk || ncand > m_free) {
+    // block 0 first, the own block last (every candidate lies between)
+    int n = 1;
+    if (l == 0) selv[0] = 0;
+    if (need_topk && m_free > 0) {
+      constexpr int PER = 16;  // key slots per lane (ncand <= 1022)
+      const int nper = (ncand + kWave - 1) / kWave;  // slots in use (wave-uniform)
+      unsigned long long key[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = 1 + l + i * kWave;
+        key[i] = (i < nper && j <= ncand)
+                     ? ((unsigned long long)__float_as_uint(imp[j]) << 10) | (unsigned)(1023 - j)
+                     : 0ull;
+      }
+      unsigned long long prefix = 0ull;
+      for (int bit = 41; bit >= 0; --bit) {
+        const unsigned long long trial = prefix | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (i < nper) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= trial));
+        if (cnt >= m_free) prefix = trial;
+      }
+      // exactly m_free keys are >= prefix (the keys are unique)
+      const unsigned long long below = l == 0 ? 0ull : (~0ull >> (kWave - l));
+      int base = 1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (i >= nper) break;
+        const bool ch = key[i] >= prefix && key[i] != 0ull;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(ch);
+        if (ch) selv[base + __popcll(bal & below)] = 1 + l + i * kWave;
+        base += __popcll(bal);
+      }
+      n = base;
+    }
+    if (l == 0 && own > 0) selv[n] = own;
+    if (l == 0) *nsel = n + (own > 0 ? 1 : 0);
+    return;
+  }
+  // every candidate is taken: 0, 1 .. own-1, own
+  for (int j = l; j <= own; j += kWave) selv[j] = j;
+  if (l == 0) *nsel = own + 1;
 }
 }  // namespace
 
@@ -263,48 +330,7 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
   }
 
   // ---- 3. top-k (wave 0)
-  if (w == 0) {
-    const int ncand = max(own - 1, 0);              // candidates 1 .. own-1
-    const int m_free = topk - (own == 0 ? 1 : 2);
-    int n = 0;
-    if (l == 0) {
-      selv[n++] = 0;
-      if (own > 0) selv[n++] = own;
-    }
-    n = __shfl(n, 0);
-    if (need_topk) {
-      if (ncand <= m_free) {
-        for (int j = 1 + l; j <= ncand; j += kWave) selv[n + j - 1] = j;
-        n += ncand;
-      } else {
-        constexpr int PER = 16;  // candidates per lane (ncand <= 1022)
-        unsigned long long key[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int j = 1 + l + i * kWave;
-          key[i] = j <= ncand ? ((unsigned long long)__float_as_uint(imp[j]) << 32) | (0xffffffffu - (unsigned)j)
-                              : 0ull;
-        }
-        for (int r = 0; r < m_free; ++r) {
-          unsigned long long best = 0ull;
-#pragma unroll
-          for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
-          best = wave_max_u64(best);
-#pragma unroll
-          for (int i = 0; i < PER; ++i)
-            if (key[i] == best) key[i] = 0ull;  // keys are unique (the index field)
-          if (l == 0) selv[n + r] = (int)(0xffffffffu - (unsigned)best);
-        }
-        n += m_free;
-      }
-    }
-    // ascending order: lane i < n takes selv[i] and writes it at its rank
-    int v = l < n ? selv[l] : 0x7fffffff;
-    int rank = 0;
-    for (int i = 0; i < n; ++i) rank += __shfl(v, i) < v;
-    if (l < n) selv[rank] = v;  // all reads above precede (shuffles of registers)
-    if (l == 0) *nsel = n;
-  }
+  if (w == 0) topk_wave(imp, own, topk, need_topk, l, selv, nsel);
   __syncthreads();
   // indices written in ascending order once selv is sorted
   if (a.indices != nullptr && w == 0 && l < topk) {
@@ -473,8 +499,359 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16: the same step on 16x16x32 MFMA tiles.  Per 64-key block a wave
+// computes S^T = K Q^T (16 keys x 16 head columns per tile; the G query
+// heads of the group fill the first G columns, the rest are zero) and then
+// O^T += V^T P^T for each branch (16 channels x 16 head columns per tile).
+// The keys of the four score tiles are permuted (dkey) so that a lane's four
+// scores of tiles 2h and 2h+1 are the eight consecutive keys 32h + 8a ..
+// +7 that the P V step contracts in its k step h: the bf16 probabilities
+// become the P^T operand without any lane exchange, and each head's running
+// maximum, sum and output live in the lanes of its column.  The V rows are
+// transposed through a per-wave LDS tile (64 keys per channel row).
+//
+// Work split: wave 0 computes the compressed branch (pooled keys in chunks
+// of 64, the same tile routine) and the importance and top-k while the
+// other waves walk the window's blocks (the own block and block 0, which are
+// always selected, also feed the selection branch there); after one barrier
+// all waves walk the remaining selected blocks.
+namespace {
+template <int D>
+struct DecM {
+  static constexpr int NW = D == 64 ? 8 : 4;
+  static constexpr int NT = NW * kWave;
+  static constexpr int KS = D / 32;       // k steps of Q K
+  static constexpr int MT = D / 16;       // channel tiles of P V
+  static constexpr int VST = kBlock + 8;  // elements per channel row of a V^T tile
+  static constexpr int VQ = D / 32;       // (key quad, 8-channel chunk) units per lane
+};
+
+struct DecMLds {
+  // float offsets into the dynamic LDS block
+  int vt, mrg, ml, sc, imp, ocmp, ints, total_floats;
+};
+
+__host__ __device__ inline DecMLds dec_mfma_lds(int G, int D, int NW, int ncap) {
+  DecMLds o;
+  const int vt_f = NW * D * (kBlock + 8) / 2;  // per-wave bf16 V^T tiles [D][VST]
+  const int mrg_f = NW * 2 * G * D;            // per-wave partial outputs [NW][2][G][D]
+  const int ml_f = NW * 2 * G * 2;             // their (max, sum) [NW][2][G][2]
+  o.vt = 0;
+  o.mrg = 0;  // the merge reuses the tiles after the last block
+  o.ml = mrg_f;
+  const int end = al4(vt_f > mrg_f + ml_f ? vt_f : mrg_f + ml_f);
+  o.sc = end;                       // scaled compressed scores [G][ncap]
+  o.imp = al4(o.sc + G * ncap);     // importance [ncap]
+  o.ocmp = al4(o.imp + ncap);       // normalised o_cmp [G][D]
+  o.ints = al4(o.ocmp + G * D);     // selv [32], nsel, blist [32], nbl
+  o.total_floats = o.ints + 66;
+  return o;
+}
+
+// row of score tile u (0..3) at tile row i (0..15) -> key within the block
+__device__ __forceinline__ int dkey(int u, int i) {
+  return 32 * (u >> 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(bf16 lo, bf16 hi) {
+  return (unsigned)__builtin_bit_cast(unsigned short, lo) |
+         ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+}
+}  // namespace
+
+template <int D, int G>
+__global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, DecodeArgs a) {
+  typedef bf16 T;
+  constexpr int NW = DecM<D>::NW, NT = DecM<D>::NT, KS = DecM<D>::KS, MT = DecM<D>::MT;
+  constexpr int VST = DecM<D>::VST, VQ = DecM<D>::VQ;
+  static_assert(G <= 16, "the heads of a group fill at most one 16-column tile");
+  const float NINF = -__builtin_inff();
+  const int bg = blockIdx.x;
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave;
+  const int col = l & 15, a4 = l >> 4;
+  const int Lmax = s.T, ncap = Lmax / kBlock;
+  const int L = min(max(a.lens[b], 1), Lmax);  // lengths outside [1, Lmax] are clamped
+  const int t = L - 1, own = t / kBlock, nc = L / kBlock;
+  const float c1 = s.scale * kLog2e;
+  const bool sel_on = !(s.flags & 2u), cmp_on = !(s.flags & 1u), win_on = !(s.flags & 4u);
+  const bool need_topk = sel_on || a.indices != nullptr;
+  const bool need_cmp = cmp_on || need_topk;
+  const int topk = s.topk, W = s.W;
+  const int jw_lo = win_on ? max(0, t - W + 1) / kBlock : own + 1;
+  const DecMLds lay = dec_mfma_lds(G, D, NW, ncap);
+
+  extern __shared__ __align__(16) float sm[];
+  T* vt = reinterpret_cast<T*>(sm + lay.vt) + (size_t)w * D * VST;  // this wave's V^T tile
+  float* sc = sm + lay.sc;
+  float* imp = sm + lay.imp;
+  float* ocmp = sm + lay.ocmp;
+  int* ints = reinterpret_cast<int*>(sm + lay.ints);
+  int* selv = ints;       // [32]
+  int* nsel = ints + 32;  // [1]
+  int* blist = ints + 33; // [32]
+  int* nbl = ints + 65;   // [1]
+
+  const size_t row = (size_t)s.Hkv * D;  // elements between consecutive positions
+  const T* kc = (const T*)a.kcache + (size_t)b * Lmax * row + (size_t)g * D;
+  const T* vc = (const T*)a.vcache + (size_t)b * Lmax * row + (size_t)g * D;
+  const T* kp = (const T*)a.kcmp + (size_t)b * ncap * row + (size_t)g * D;
+  const T* vp = (const T*)a.vcmp + (size_t)b * ncap * row + (size_t)g * D;
+
+  // Q^T as the B operand: lane (column col, group a4) holds Q[col][32 ks + 8 a4 ..]
+  const T* q = (const T*)a.q + ((size_t)b * s.Hq + (size_t)g * G) * D;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = col < G ? Frag<T>::load(q + (size_t)col * D + 32 * ks + 8 * a4) : Frag<T>::zero();
+
+  // per branch (0: selection, 1: window; wave 0 uses slot 0 for the
+  // compressed branch first): running maximum (log2 units) and this lane's
+  // part of the sum, per head column; O^T tiles (lane: channels 16 mt + 4 a4
+  // + r of head col)
+  float m[2], ls[2];
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    m[br] = NINF;
+    ls[br] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[br][mt] = zero4();
+  }
+
+  // One block of 64 keys: kb / vb point at its first key row; keys with
+  // block index >= kvalid are not read; window keys are those with block
+  // index >= wkey0.  scw (wave 0's compressed pass) receives the scaled
+  // scores of the G heads.
+  auto run_block = [&](const T* kb, const T* vb, int kvalid, int wkey0, bool do_s, bool do_w,
+                       float* scw) {
+    // V rows: unit (key quad l % 16, chunk (l / 16) + 4 v) -> four 16-byte loads
+    bf16x8 vr[VQ][4];
+#pragma unroll
+    for (int v = 0; v < VQ; ++v)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = 4 * col + kk;
+        vr[v][kk] = key < kvalid ? Frag<T>::load(vb + (size_t)key * row + 8 * (a4 + 4 * v)) : Frag<T>::zero();
+      }
+    // K as the A operand of the four score tiles
+    bf16x8 kf[4][KS];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = dkey(u, col);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[u][ks] = key < kvalid ? Frag<T>::load(kb + (size_t)key * row + 32 * ks + 8 * a4) : Frag<T>::zero();
+    }
+    f32x4 sacc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sacc[u] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[u] = mma(sacc[u], kf[u][ks], qf[ks]);
+    }
+    // V^T tile: channel row 8 c + e, keys 4 quad .. 4 quad + 3 in one 8-byte store
+#pragma unroll
+    for (int v = 0; v < VQ; ++v) {
+      const int c = a4 + 4 * v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint2 pr;
+        pr.x = pack_bf16x2(vr[v][0][e], vr[v][1][e]);
+        pr.y = pack_bf16x2(vr[v][2][e], vr[v][3][e]);
+        *reinterpret_cast<uint2*>(vt + (8 * c + e) * VST + 4 * col) = pr;
+      }
+    }
+    float x[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[u][r] = sacc[u][r] * c1;
+    if (scw != nullptr && col < G) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = dkey(u, 4 * a4 + r);
+          if (kidx < kvalid) scw[col * ncap + kidx] = x[u][r];
+        }
+    }
+    __builtin_amdgcn_wave_barrier();  // the tile's rows come from other lanes
+    // V^T as the A operand: lane (channel 16 mt + col, group a4) holds keys
+    // 32 h + 8 a4 .. +7
+    bf16x8 vf[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        vf[mt][h] = *reinterpret_cast<const bf16x8*>(vt + (16 * mt + col) * VST + 32 * h + 8 * a4);
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      if (br == 0 ? !do_s : !do_w) continue;
+      const int klo = br == 0 ? 0 : wkey0;  // first key of the branch in this block
+      float bm = NINF;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = dkey(u, 4 * a4 + r);
+          if (kidx < kvalid && kidx >= klo) bm = fmaxf(bm, x[u][r]);
+        }
+      bm = xmax4(bm);
+      const float mn = fmaxf(m[br], bm);
+      const float al = m[br] == NINF ? 0.f : fast_exp2(m[br] - mn);
+      float p[4][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = dkey(u, 4 * a4 + r);
+          p[u][r] = (kidx < kvalid && kidx >= klo) ? fast_exp2(x[u][r] - mn) : 0.f;
+          psum += p[u][r];
+        }
+      ls[br] = ls[br] * al + psum;
+      m[br] = mn;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[h][e] = (bf16)p[2 * h + (e >> 2)][e & 3];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[br][mt] = acc[br][mt] * al;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[br][mt] = mma(acc[br][mt], vf[mt][h], pf[h]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // tile reads done before the next block's stores
+  };
+
+  if (!need_cmp && tid == 0) *nbl = 0;
+
+  // ---- window blocks (waves 1 .. NW-1; every wave when wave 0 has no
+  // compressed work)
+  const int wfirst = need_cmp ? 1 : 0;
+  if (win_on && w >= wfirst) {
+    for (int j = jw_lo + (w - wfirst); j <= own; j += NW - wfirst) {
+      const size_t off = (size_t)j * kBlock * row;
+      run_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), t - W + 1 - j * kBlock,
+                sel_on && (j == 0 || j == own), true, nullptr);
+    }
+  }
+
+  // ---- wave 0: compressed branch, importance, top-k, the selection list
+  if (w == 0 && need_cmp) {
+    for (int ci = 0; ci * kBlock < nc; ++ci) {
+      const size_t off = (size_t)ci * kBlock * row;
+      run_block(kp + off, vp + off, min(kBlock, nc - ci * kBlock), 0, true, false, sc + ci * kBlock);
+    }
+    if (nc > 0) {
+      const float lt = xsum4(ls[0]);
+      const float lse = m[0] + __log2f(lt);  // per head column (log2 units)
+      if (col < G) {
+        const float il = 1.f / lt;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4*>(ocmp + col * D + 16 * mt + 4 * a4) = acc[0][mt] * il;
+      }
+      float lse_h[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        lse_h[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse), h));
+      __builtin_amdgcn_wave_barrier();  // scores from every lane are in LDS
+      for (int j = l; j < nc; j += kWave) {
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) sum += fast_exp2(sc[h * ncap + j] - lse_h[h]);
+        imp[j] = sum;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    m[0] = NINF;
+    ls[0] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[0][mt] = zero4();
+    topk_wave(imp, own, topk, need_topk, l, selv, nsel);
+    __builtin_amdgcn_wave_barrier();
+    const int n = *nsel;
+    if (a.indices != nullptr && l < topk) a.indices[((size_t)b * s.Hkv + g) * topk + l] = l < n ? selv[l] : -1;
+    {
+      // the selected blocks still to walk (block 0 and the own block of the
+      // window range were walked above), ascending, compacted by ballot
+      const int j = l < n ? selv[l] : 0;
+      const bool keep = sel_on && l < n && !(win_on && j >= jw_lo && (j == 0 || j == own));
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
+      const unsigned long long below = l == 0 ? 0ull : (~0ull >> (kWave - l));
+      if (keep) blist[__popcll(bal & below)] = j;
+      if (l == 0) *nbl = __popcll(bal);
+    }
+  }
+  __syncthreads();
+
+  // ---- the remaining selected blocks, every wave (from the last wave down)
+  const int nb = *nbl;
+  for (int k = NW - 1 - w; k < nb; k += NW) {
+    const int j = blist[k];
+    const size_t off = (size_t)j * kBlock * row;
+    run_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), 0, true, false, nullptr);
+  }
+  __syncthreads();  // all waves past their last use of the V^T tiles
+
+  // ---- combine the waves, gate, write
+  float* mrg = sm + lay.mrg;  // [NW][2][G][D]
+  float* ml = sm + lay.ml;    // [NW][2][G][2]
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    const float lt = xsum4(ls[br]);
+    if (col < G) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4*>(mrg + ((w * 2 + br) * G + col) * D + 16 * mt + 4 * a4) = acc[br][mt];
+      if (a4 == 0) {
+        ml[((w * 2 + br) * G + col) * 2 + 0] = m[br];
+        ml[((w * 2 + br) * G + col) * 2 + 1] = lt;
+      }
+    }
+  }
+  __syncthreads();
+  const T* gates = (const T*)a.gates + ((size_t)b * s.Hq + (size_t)g * G) * 3;
+  T* out = (T*)a.out + ((size_t)b * s.Hq + (size_t)g * G) * D;
+  for (int e = tid; e < G * D; e += NT) {
+    const int h = e / D, d = e % D;
+    float res = 0.f;
+    for (int br = 0; br < 2; ++br) {
+      if (br == 0 && !sel_on) continue;
+      if (br == 1 && !win_on) continue;
+      float M = NINF;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[((ww * 2 + br) * G + h) * 2]);
+      if (M == NINF) continue;  // no key of this branch (cannot happen for a valid row)
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = ml[((ww * 2 + br) * G + h) * 2];
+        if (mw == NINF) continue;  // this wave saw no key of the branch
+        const float sc_w = fast_exp2(mw - M);
+        den += sc_w * ml[((ww * 2 + br) * G + h) * 2 + 1];
+        num += sc_w * mrg[((ww * 2 + br) * G + h) * D + d];
+      }
+      res += to_f32(gates[h * 3 + 1 + br]) * (num / den);
+    }
+    if (cmp_on && nc > 0) res += to_f32(gates[h * 3]) * ocmp[e];
+    out[e] = from_f32<T>(res);
+  }
+}
+
 size_t decode_lds_bytes(bool is_bf16, const Shape& s) {
   const int ncap = s.T / kBlock;
+  if (is_bf16) {
+    const int NW = s.D == 64 ? DecM<64>::NW : DecM<128>::NW;
+    return (size_t)dec_mfma_lds(s.G, s.D, NW, ncap).total_floats * 4;
+  }
   const int wmax = (s.W - 1) / kBlock + 2 < ncap ? (s.W - 1) / kBlock + 2 : ncap;
   const int es = is_bf16 ? 2 : 4;
   const int NW = (is_bf16 && s.D == 64) ? DecCfg<bf16, 64>::NW : DecCfg<float, 64>::NW;
@@ -491,6 +868,29 @@ static hipError_t launch_dec(const Shape& s, const DecodeArgs& a, hipStream_t st
   }
   hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(s.B * s.Hkv), dim3(DecCfg<T, D>::NT), lds, st, s, a);
   return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_dec_mfma(const Shape& s, const DecodeArgs& a, hipStream_t st) {
+  const size_t lds = decode_lds_bytes(true, s);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<D, G>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(s.B * s.Hkv), dim3(DecM<D>::NT), lds, st, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dec_mfma_g(const Shape& s, const DecodeArgs& a, hipStream_t st) {
+  switch (s.G) {
+    case 1: return launch_dec_mfma<D, 1>(s, a, st);
+    case 2: return launch_dec_mfma<D, 2>(s, a, st);
+    case 4: return launch_dec_mfma<D, 4>(s, a, st);
+    case 8: return launch_dec_mfma<D, 8>(s, a, st);
+    default: return launch_dec_mfma<D, 16>(s, a, st);
+  }
 }
 
 template <typename T, int D>
@@ -510,8 +910,8 @@ hipError_t launch_decode(bool is_bf16, const Shape& s, const void* q, const void
                          hipStream_t st) {
   DecodeArgs a{q, kcache, vcache, kcmp, vcmp, lens, gates, out, indices};
   if (is_bf16) {
-    if (s.D == 64) return launch_dec_g<bf16, 64>(s, a, st);
-    return launch_dec_g<bf16, 128>(s, a, st);
+    if (s.D == 64) return launch_dec_mfma_g<64>(s, a, st);
+    return launch_dec_mfma_g<128>(s, a, st);
   }
   return launch_dec_g<float, 64>(s, a, st);
 }
