@@ -622,14 +622,9 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
     for (int mt = 0; mt < MT; ++mt) acc[br][mt] = zero4();
   }
 
-  // One block of 64 keys: kb / vb point at its first key row; keys with
-  // block index >= kvalid are not read; window keys are those with block
-  // index >= wkey0.  scw (wave 0's compressed pass) receives the scaled
-  // scores of the G heads.
-  auto run_block = [&](const T* kb, const T* vb, int kvalid, int wkey0, bool do_s, bool do_w,
-                       float* scw) {
-    // V rows: unit (key quad l % 16, chunk (l / 16) + 4 v) -> four 16-byte loads
-    bf16x8 vr[VQ][4];
+  // ---- pieces of one 64-key block
+  // loads of the block's V rows (unit: key quad l % 16, chunk (l / 16) + 4 v)
+  auto load_v = [&](bf16x8 (&vr)[VQ][4], const T* vb, int kvalid) {
 #pragma unroll
     for (int v = 0; v < VQ; ++v)
 #pragma unroll
@@ -637,8 +632,9 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
         const int key = 4 * col + kk;
         vr[v][kk] = key < kvalid ? Frag<T>::load(vb + (size_t)key * row + 8 * (a4 + 4 * v)) : Frag<T>::zero();
       }
-    // K as the A operand of the four score tiles
-    bf16x8 kf[4][KS];
+  };
+  // loads of K as the A operand of the four score tiles
+  auto load_k = [&](bf16x8 (&kf)[4][KS], const T* kb, int kvalid) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int key = dkey(u, col);
@@ -646,14 +642,20 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
       for (int ks = 0; ks < KS; ++ks)
         kf[u][ks] = key < kvalid ? Frag<T>::load(kb + (size_t)key * row + 32 * ks + 8 * a4) : Frag<T>::zero();
     }
-    f32x4 sacc[4];
+  };
+  // scaled scores: x[u][r] for key dkey(u, 4 a4 + r), head col (log2 units)
+  auto scores = [&](f32x4 (&x)[4], const bf16x8 (&kf)[4][KS]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      sacc[u] = zero4();
+      f32x4 c = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[u] = mma(sacc[u], kf[u][ks], qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) c = mma(c, kf[u][ks], qf[ks]);
+      x[u] = c * c1;
     }
-    // V^T tile: channel row 8 c + e, keys 4 quad .. 4 quad + 3 in one 8-byte store
+  };
+  // V^T tile: channel row 8 c + e, keys 4 quad .. 4 quad + 3 in one 8-byte
+  // store; then the tile is read back by other lanes of the wave
+  auto stage_vt = [&](const bf16x8 (&vr)[VQ][4]) {
 #pragma unroll
     for (int v = 0; v < VQ; ++v) {
       const int c = a4 + 4 * v;
@@ -665,29 +667,31 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
         *reinterpret_cast<uint2*>(vt + (8 * c + e) * VST + 4 * col) = pr;
       }
     }
-    float x[4][4];
+    __builtin_amdgcn_wave_barrier();
+  };
+  // O^T += V^T P^T from the staged tile: lane (channel 16 mt + col, group a4)
+  // holds keys 32 h + 8 a4 .. +7 of the A operand; pf[h] is the P^T operand
+  auto pv = [&](f32x4 (&o)[MT], const bf16x8 (&pf)[2], float al) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[u][r] = sacc[u][r] * c1;
-    if (scw != nullptr && col < G) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kidx = dkey(u, 4 * a4 + r);
-          if (kidx < kvalid) scw[col * ncap + kidx] = x[u][r];
-        }
-    }
-    __builtin_amdgcn_wave_barrier();  // the tile's rows come from other lanes
-    // V^T as the A operand: lane (channel 16 mt + col, group a4) holds keys
-    // 32 h + 8 a4 .. +7
-    bf16x8 vf[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 c = o[mt] * al;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        vf[mt][h] = *reinterpret_cast<const bf16x8*>(vt + (16 * mt + col) * VST + 32 * h + 8 * a4);
+        c = mma(c, *reinterpret_cast<const bf16x8*>(vt + (16 * mt + col) * VST + 32 * h + 8 * a4), pf[h]);
+      o[mt] = c;
+    }
+  };
+  // one key block of the selection (br 0) and / or window (br 1) branch;
+  // keys with block index >= kvalid are not read, window keys are those at
+  // block index >= wkey0
+  auto attend_block = [&](const T* kb, const T* vb, int kvalid, int wkey0, bool do_s, bool do_w) {
+    bf16x8 vr[VQ][4];
+    bf16x8 kf[4][KS];
+    load_v(vr, vb, kvalid);
+    load_k(kf, kb, kvalid);
+    f32x4 x[4];
+    scores(x, kf);
+    stage_vt(vr);
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
       if (br == 0 ? !do_s : !do_w) continue;
@@ -703,29 +707,22 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
       bm = xmax4(bm);
       const float mn = fmaxf(m[br], bm);
       const float al = m[br] == NINF ? 0.f : fast_exp2(m[br] - mn);
-      float p[4][4];
+      // probabilities straight into the P^T operand of k step u / 2,
+      // element 4 (u % 2) + r
+      bf16x8 pf[2];
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kidx = dkey(u, 4 * a4 + r);
-          p[u][r] = (kidx < kvalid && kidx >= klo) ? fast_exp2(x[u][r] - mn) : 0.f;
-          psum += p[u][r];
+          const float pvl = (kidx < kvalid && kidx >= klo) ? fast_exp2(x[u][r] - mn) : 0.f;
+          psum += pvl;
+          pf[u >> 1][4 * (u & 1) + r] = (bf16)pvl;
         }
       ls[br] = ls[br] * al + psum;
       m[br] = mn;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[h][e] = (bf16)p[2 * h + (e >> 2)][e & 3];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[br][mt] = acc[br][mt] * al;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[br][mt] = mma(acc[br][mt], vf[mt][h], pf[h]);
-      }
+      pv(acc[br], pf, al);
     }
     __builtin_amdgcn_wave_barrier();  // tile reads done before the next block's stores
   };
@@ -738,26 +735,55 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
   if (win_on && w >= wfirst) {
     for (int j = jw_lo + (w - wfirst); j <= own; j += NW - wfirst) {
       const size_t off = (size_t)j * kBlock * row;
-      run_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), t - W + 1 - j * kBlock,
-                sel_on && (j == 0 || j == own), true, nullptr);
+      attend_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), t - W + 1 - j * kBlock,
+                   sel_on && (j == 0 || j == own), true);
     }
   }
 
-  // ---- wave 0: compressed branch, importance, top-k, the selection list
+  // ---- wave 0: compressed scores (two chunks of 64 pooled keys in flight
+  // at a time), their log-sum-exp per head, the importance, the top-k and the
+  // list of selected blocks still to walk.  The compressed output (P V over
+  // the pooled values) is left for after the barrier: the top-k does not
+  // need it.
+  const int nchunk = (nc + kBlock - 1) / kBlock;
+  float lse = 0.f;  // per head column, log2 units
   if (w == 0 && need_cmp) {
-    for (int ci = 0; ci * kBlock < nc; ++ci) {
-      const size_t off = (size_t)ci * kBlock * row;
-      run_block(kp + off, vp + off, min(kBlock, nc - ci * kBlock), 0, true, false, sc + ci * kBlock);
+    float mc = NINF, lc = 0.f;
+    auto chunk_stats = [&](const bf16x8 (&kf)[4][KS], int ci) {
+      const int kvalid = min(kBlock, nc - ci * kBlock);
+      f32x4 x[4];
+      scores(x, kf);
+      float bm = NINF;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = dkey(u, 4 * a4 + r);
+          if (kidx < kvalid) {
+            bm = fmaxf(bm, x[u][r]);
+            if (col < G) sc[col * ncap + ci * kBlock + kidx] = x[u][r];
+          }
+        }
+      bm = xmax4(bm);
+      const float mn = fmaxf(mc, bm);
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (dkey(u, 4 * a4 + r) < kvalid) psum += fast_exp2(x[u][r] - mn);
+      lc = (mc == NINF ? 0.f : lc * fast_exp2(mc - mn)) + psum;
+      mc = mn;
+    };
+    for (int ci = 0; ci < nchunk; ci += 2) {
+      bf16x8 kA[4][KS], kB[4][KS];
+      load_k(kA, kp + (size_t)ci * kBlock * row, min(kBlock, nc - ci * kBlock));
+      if (ci + 1 < nchunk) load_k(kB, kp + (size_t)(ci + 1) * kBlock * row, min(kBlock, nc - (ci + 1) * kBlock));
+      chunk_stats(kA, ci);
+      if (ci + 1 < nchunk) chunk_stats(kB, ci + 1);
     }
     if (nc > 0) {
-      const float lt = xsum4(ls[0]);
-      const float lse = m[0] + __log2f(lt);  // per head column (log2 units)
-      if (col < G) {
-        const float il = 1.f / lt;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(ocmp + col * D + 16 * mt + 4 * a4) = acc[0][mt] * il;
-      }
+      lse = mc + __log2f(xsum4(lc));
       float lse_h[G];
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -771,10 +797,6 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
       }
       __builtin_amdgcn_wave_barrier();
     }
-    m[0] = NINF;
-    ls[0] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[0][mt] = zero4();
     topk_wave(imp, own, topk, need_topk, l, selv, nsel);
     __builtin_amdgcn_wave_barrier();
     const int n = *nsel;
@@ -797,7 +819,37 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
   for (int k = NW - 1 - w; k < nb; k += NW) {
     const int j = blist[k];
     const size_t off = (size_t)j * kBlock * row;
-    run_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), 0, true, false, nullptr);
+    attend_block(kc + off, vc + off, min(kBlock, t - j * kBlock + 1), 0, true, false);
+  }
+  // ---- wave 0: the compressed output, o_cmp = sum_j p_j Vc_j with
+  // p_j = 2^(score - lse) from the stored scores
+  if (w == 0 && cmp_on && nc > 0) {
+    f32x4 oc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oc[mt] = zero4();
+    for (int ci = 0; ci < nchunk; ++ci) {
+      const int kvalid = min(kBlock, nc - ci * kBlock);
+      bf16x8 vr[VQ][4];
+      load_v(vr, vp + (size_t)ci * kBlock * row, kvalid);
+      // P^T operand: lane (head col, group a4), k step h: keys 32 h + 8 a4 + e
+      bf16x8 pf[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kidx = 32 * h + 8 * a4 + e;
+          const float pvl = (col < G && kidx < kvalid) ? fast_exp2(sc[col * ncap + ci * kBlock + kidx] - lse) : 0.f;
+          pf[h][e] = (bf16)pvl;
+        }
+      stage_vt(vr);
+      pv(oc, pf, 1.f);
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (col < G) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4*>(ocmp + col * D + 16 * mt + 4 * a4) = oc[mt];
+    }
   }
   __syncthreads();  // all waves past their last use of the V^T tiles
 
