@@ -137,6 +137,40 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return swap(v, true);
 }
 
+// Radix select over PER key slots per lane (empty slots hold 0): writes the
+// chosen candidates (keys >= the m-th largest) to selv[1 ..] in ascending
+// block order (slot i of lane l is block 1 + l + 64 i) and returns 1 + m.
+template <int PER>
+__device__ __forceinline__ int radix_pick(const float* imp, int ncand, int m, int l, int* selv) {
+  unsigned long long key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = 1 + l + i * kWave;
+    key[i] = j <= ncand ? ((unsigned long long)__float_as_uint(imp[j]) << 10) | (unsigned)(1023 - j) : 0ull;
+  }
+  // every trial has a bit set, so the empty slots (0) never count
+  unsigned long long prefix = 0ull;
+  for (int bit = 41; bit >= 0; --bit) {
+    const unsigned long long trial = prefix | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= trial));
+    if (cnt >= m) prefix = trial;
+  }
+  // exactly m keys are >= prefix (the keys are unique, prefix >= 1)
+  const unsigned long long below = l == 0 ? 0ull : (~0ull >> (kWave - l));
+  int base = 1;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool ch = key[i] >= prefix;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(ch);
+    if (ch) selv[base + __popcll(bal & below)] = 1 + l + i * kWave;
+    base += __popcll(bal);
+  }
+  return base;
+}
+
+
 // Top-k of one (sequence, group), run by one wave (lane l): the forced blocks
 // 0 and own, then the m_free largest importances among blocks 1 .. own-1
 // (ties to the lower index), or every candidate when there are no more than
@@ -161,37 +195,11 @@ __device__ void topk_wave(const float* imp, int own, int topk, bool need_topk, i
     int n = 1;
     if (l == 0) selv[0] = 0;
     if (need_topk && m_free > 0) {
-      constexpr int PER = 16;  // key slots per lane (ncand <= 1022)
-      const int nper = (ncand + kWave - 1) / kWave;  // slots in use (wave-uniform)
-      unsigned long long key[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int j = 1 + l + i * kWave;
-        key[i] = (i < nper && j <= ncand)
-                     ? ((unsigned long long)__float_as_uint(imp[j]) << 10) | (unsigned)(1023 - j)
-                     : 0ull;
-      }
-      unsigned long long prefix = 0ull;
-      for (int bit = 41; bit >= 0; --bit) {
-        const unsigned long long trial = prefix | (1ull << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (i < nper) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= trial));
-        if (cnt >= m_free) prefix = trial;
-      }
-      // exactly m_free keys are >= prefix (the keys are unique)
-      const unsigned long long below = l == 0 ? 0ull : (~0ull >> (kWave - l));
-      int base = 1;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (i >= nper) break;
-        const bool ch = key[i] >= prefix && key[i] != 0ull;
-        const unsigned long long bal = __builtin_amdgcn_ballot_w64(ch);
-        if (ch) selv[base + __popcll(bal & below)] = 1 + l + i * kWave;
-        base += __popcll(bal);
-      }
-      n = base;
+      // key slots per lane: ncand <= 1022 (caches of at most 65536 positions)
+      if (ncand <= 2 * kWave) n = radix_pick<2>(imp, ncand, m_free, l, selv);
+      else if (ncand <= 4 * kWave) n = radix_pick<4>(imp, ncand, m_free, l, selv);
+      else if (ncand <= 8 * kWave) n = radix_pick<8>(imp, ncand, m_free, l, selv);
+      else n = radix_pick<16>(imp, ncand, m_free, l, selv);
     }
     if (l == 0 && own > 0) selv[n] = own;
     if (l == 0) *nsel = n + (own > 0 ? 1 : 0);

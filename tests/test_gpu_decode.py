@@ -99,6 +99,10 @@ CASES = [
     (W13.with_(n_q_heads=16, n_kv_heads=2), 2, 2048, [900, 2048]),       # G = 8
     (WMQA, 2, 2048, [512, 1500]),                                        # G = 16
     (WTINY, 3, 1024, [10, 300, 1024]),                                   # fp32
+    # long caches: 2, 4, 8 and 16 top-k key slots per lane (candidates up to
+    # 126, 254, 510 and 1022)
+    (W340, 3, 32768, [8000, 16000, 32768]),
+    (W340.with_(top_k=8), 1, 65536, [65536]),
 ]
 
 
