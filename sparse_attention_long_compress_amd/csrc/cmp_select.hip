@@ -81,7 +81,8 @@ __device__ __forceinline__ void sort_desc(uint32_t (&a)[N]) {
 
 template <typename T, int D, int G>
 struct K2Cfg {
-  static constexpr int P = (256 / G) < 64 ? (256 / G) : 64;  // positions per tile
+  // positions per tile: 256 rows at head_dim 64, 128 at 128 (capped at one block)
+  static constexpr int P = ((D == 64 ? 256 : 128) / G) < 64 ? ((D == 64 ? 256 : 128) / G) : 64;
   static constexpr int R = P * G;                            // rows per tile
   static constexpr int NW = (R / 16) < 8 ? (R / 16) : 8;     // waves (at least one column group each)
   static constexpr int NT = NW * 64;
@@ -89,9 +90,10 @@ struct K2Cfg {
   static constexpr int CGW = RWV / 16;                       // column groups per wave
   static constexpr int CPW = 64 / NW;                        // top-k candidates per wave and chunk
   static constexpr int KS = D / 32, MT = D / 16;
-  // minimum waves per SIMD (launch bound): 4 at head_dim 64 -- two 8-wave
-  // workgroups per CU, at most 128 VGPRs; at 128 the registers allow one
-  static constexpr int MIN_WAVES_EU = (D == 64 && NW == 8) ? 4 : 1;
+  // minimum waves per SIMD (launch bound): 4 with 8 waves -- two workgroups
+  // per CU, at most 128 VGPRs (at head_dim 128 the tile has half as many
+  // positions, one column group per wave, so that it fits)
+  static constexpr int MIN_WAVES_EU = (NW == 8) ? 4 : 1;
   static constexpr int KST = D + 8;   // LDS row stride of the pooled-key chunk
   static constexpr int VST = 64 + 8;  // LDS row stride of the pooled-value chunk
 };
