@@ -98,6 +98,9 @@ CASES = [
     (W13, 3, 2048, [100, 1024, 2048]),
     (W13.with_(n_q_heads=16, n_kv_heads=2), 2, 2048, [900, 2048]),       # G = 8
     (WMQA, 2, 2048, [512, 1500]),                                        # G = 16
+    (W13.with_(n_q_heads=4, n_kv_heads=4), 3, 1024, [64, 500, 1000]),    # head_dim 128, G = 1
+    (W13.with_(n_q_heads=8, n_kv_heads=4), 3, 1024, [1, 130, 1024]),     # head_dim 128, G = 2
+    (W13.with_(top_k=3, window=100), 3, 2048, [65, 777, 2048]),          # head_dim 128, short window
     (WTINY, 3, 1024, [10, 300, 1024]),                                   # fp32
     # long caches: 2, 4, 8 and 16 top-k key slots per lane (candidates up to
     # 126, 254, 510 and 1022)
