@@ -520,11 +520,12 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
 // maximum, sum and output live in the lanes of its column.  The V rows are
 // transposed through a per-wave LDS tile (64 keys per channel row).
 //
-// Work split: wave 0 computes the compressed branch (pooled keys in chunks
-// of 64, the same tile routine) and the importance and top-k while the
-// other waves walk the window's blocks (the own block and block 0, which are
-// always selected, also feed the selection branch there); after one barrier
-// all waves walk the remaining selected blocks.
+// Work split: wave 0 computes the compressed scores (pooled keys in chunks
+// of 64, the same score tiles), their log-sum-exp, the importance and the
+// top-k while the other waves walk the window's blocks (the own block and
+// block 0, which are always selected, also feed the selection branch there);
+// after one barrier all waves walk the remaining selected blocks and wave 0
+// also the compressed output (P V over the pooled values).
 namespace {
 template <int D>
 struct DecM {
@@ -566,6 +567,14 @@ __device__ __forceinline__ int dkey(int u, int i) {
 __device__ __forceinline__ unsigned pack_bf16x2(bf16 lo, bf16 hi) {
   return (unsigned)__builtin_bit_cast(unsigned short, lo) |
          ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+}
+
+// hand-off of LDS data between the lanes of one wave: the wave's LDS
+// accesses execute in program order, so only the compiler must be kept from
+// moving accesses across this point
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 }  // namespace
 
@@ -616,10 +625,9 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = col < G ? Frag<T>::load(q + (size_t)col * D + 32 * ks + 8 * a4) : Frag<T>::zero();
 
-  // per branch (0: selection, 1: window; wave 0 uses slot 0 for the
-  // compressed branch first): running maximum (log2 units) and this lane's
-  // part of the sum, per head column; O^T tiles (lane: channels 16 mt + 4 a4
-  // + r of head col)
+  // per branch (0: selection, 1: window): running maximum (log2 units) and
+  // this lane's part of the sum, per head column; O^T tiles (lane: channels
+  // 16 mt + 4 a4 + r of head col)
   float m[2], ls[2];
   f32x4 acc[2][MT];
 #pragma unroll
@@ -675,7 +683,7 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
         *reinterpret_cast<uint2*>(vt + (8 * c + e) * VST + 4 * col) = pr;
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
   };
   // O^T += V^T P^T from the staged tile: lane (channel 16 mt + col, group a4)
   // holds keys 32 h + 8 a4 .. +7 of the A operand; pf[h] is the P^T operand
@@ -732,7 +740,7 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
       m[br] = mn;
       pv(acc[br], pf, al);
     }
-    __builtin_amdgcn_wave_barrier();  // tile reads done before the next block's stores
+    wave_lds_sync();  // tile reads done before the next block's stores
   };
 
   if (!need_cmp && tid == 0) *nbl = 0;
@@ -796,17 +804,17 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
 #pragma unroll
       for (int h = 0; h < G; ++h)
         lse_h[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse), h));
-      __builtin_amdgcn_wave_barrier();  // scores from every lane are in LDS
+      wave_lds_sync();  // scores from every lane are in LDS
       for (int j = l; j < nc; j += kWave) {
         float sum = 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h) sum += fast_exp2(sc[h * ncap + j] - lse_h[h]);
         imp[j] = sum;
       }
-      __builtin_amdgcn_wave_barrier();
+      wave_lds_sync();
     }
     topk_wave(imp, own, topk, need_topk, l, selv, nsel);
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     const int n = *nsel;
     if (a.indices != nullptr && l < topk) a.indices[((size_t)b * s.Hkv + g) * topk + l] = l < n ? selv[l] : -1;
     {
@@ -851,7 +859,7 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
         }
       stage_vt(vr);
       pv(oc, pf, 1.f);
-      __builtin_amdgcn_wave_barrier();
+      wave_lds_sync();
     }
     if (col < G) {
 #pragma unroll
