@@ -90,6 +90,11 @@ CASES = [
     ("340m-gqa4", 1024, 1.0, {"batch": 3}),
     # a window range beyond 32 blocks falls back to the general kernel
     ("340m-gqa4", 2048, 1.0, {"window": 2048}),
+    # packed-selection kernel edge cases: only the forced blocks and a one-key
+    # window; a single block; top-k covering every block (all blocks are items)
+    ("340m-gqa4", 512, 0.0, {"top_k": 2, "window": 1}),
+    ("340m-gqa4", 64, 0.0, {"batch": 2}),
+    ("340m-gqa4", 1024, 0.0, {"top_k": 32, "window": 64}),
 ]
 
 
