@@ -92,8 +92,9 @@ struct K2Cfg {
   static constexpr int KS = D / 32, MT = D / 16;
   // minimum waves per SIMD (launch bound): 4 with 8 waves -- two workgroups
   // per CU, at most 128 VGPRs (at head_dim 128 the tile has half as many
-  // positions, one column group per wave, so that it fits)
-  static constexpr int MIN_WAVES_EU = (NW == 8) ? 4 : 1;
+  // positions, one column group per wave, so that it fits); fp32 fragments
+  // are twice as wide and would spill under that bound
+  static constexpr int MIN_WAVES_EU = (NW == 8 && sizeof(T) == 2) ? 4 : 1;
   static constexpr int KST = D + 8;   // LDS row stride of the pooled-key chunk
   static constexpr int VST = 64 + 8;  // LDS row stride of the pooled-value chunk
 };
