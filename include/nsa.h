@@ -258,8 +258,9 @@ nsa_status_t nsa_backward(const void* q, const void* k, const void* v, const voi
  *   out      : [B][Hq][D], overwritten.
  *   indices  : optional int32 [B][Hkv][top_k]: the selected blocks,
  *              ascending, -1 padded.
- * No workspace; the kernel's on-chip memory grows with Lmax, the query heads
- * per group and the window: NSA_ERR_UNSUPPORTED when it would exceed 160 KB. */
+ * No workspace; the kernel's on-chip memory grows with Lmax and the query
+ * heads per group (for fp32 also with the window): NSA_ERR_UNSUPPORTED when it
+ * would exceed 160 KB. */
 nsa_status_t nsa_decode(const void* q, const void* k_cache, const void* v_cache,
                         const void* k_cmp, const void* v_cmp, const int32_t* seq_lens,
                         const void* gates, const nsa_params_t* p, void* out, int32_t* indices,
