@@ -135,6 +135,11 @@ def test_decode_full_cache_size():
     run_case(W340, 16, 8192, lens, seed=14)
 
 
+def test_decode_bench_shape():
+    # the launch the decode bench times: 64 sequences, every cache full
+    run_case(W340, 64, 8192, [8192] * 64, seed=15)
+
+
 def test_decode_rejects_index_input():
     wl = W340
     dev, _ = decode_inputs(wl, 1, 128, [100], 0)
