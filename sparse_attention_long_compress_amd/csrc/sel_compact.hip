@@ -76,6 +76,12 @@ bool sel_compact_eligible(bool is_bf16, const Shape& s) {
          sel_compact_lds_bytes(s.T) <= 160 * 1024;
 }
 
+// compile-time tag of the walk's two period bodies
+template <bool B>
+struct RangeTag {
+  static constexpr bool value = B;
+};
+
 __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArgs args) {
   typedef bf16 T;
   typedef bf16x8 FragT;
@@ -345,7 +351,12 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   };
 
   unsigned long long ev = 0ull;  // blocks j_begin + 64 c .. + 63 where this wave has an item
-  for (int bi = 0; bi < nblk; ++bi) {
+  // One block period.  A wave's blocks before its register range run a
+  // body without the register-range part (scalar issue, shared by the
+  // 15 waves of a CU, bounds the walk); each period has one barrier on
+  // either path, so every wave meets the same barriers.
+  auto period = [&](int bi, auto range_tag) __attribute__((always_inline)) {
+    constexpr bool RANGE = decltype(range_tag)::value;
     if ((bi & (kWave - 1)) == 0) {
       const int jj = j_begin + bi + l;
       bool e = false;
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       pend = false;
     }
 
-    if (j >= jr_lo && j <= jr_hi) {
+    if (RANGE && j >= jr_lo && j <= jr_hi) {
       // register range of the wave's own column group
       const bool act_w = j >= jw_lo && j <= jw_hi;
       const bool inr = j >= jr_lo && j <= jr_hi;
@@ -515,7 +526,11 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         dl = xsum4(frag_sum(dp[0]) + frag_sum(dp[1]));
         pend = true;
       }
-  }
+  };
+  const int split = jr_hi >= jr_lo ? min(max(jr_lo - j_begin, 0), nblk) : nblk;
+  int bi = 0;
+  for (; bi < split; ++bi) period(bi, RangeTag<false>{});
+  for (; bi < nblk; ++bi) period(bi, RangeTag<true>{});
   // the last block's items: after every wave has finished the previous
   // block's updates
   barrier_keep_loads();
