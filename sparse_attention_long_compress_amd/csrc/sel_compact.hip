@@ -350,13 +350,16 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     }
   };
 
-  unsigned long long ev = 0ull;  // blocks j_begin + 64 c .. + 63 where this wave has an item
+  // blocks where this wave has an item: refreshed every 64 blocks, bit 0 is
+  // the current block
+  unsigned long long ev = 0ull;
   // One block period.  A wave's blocks before its register range run a
   // body without the register-range part (scalar issue, shared by the
   // 15 waves of a CU, bounds the walk); each period has one barrier on
   // either path, so every wave meets the same barriers.
-  auto period = [&](int bi, auto range_tag) __attribute__((always_inline)) {
-    constexpr bool RANGE = decltype(range_tag)::value;
+  auto period = [&](int bi, auto range_tag, auto loader_tag) __attribute__((always_inline)) {
+    constexpr bool RANGE = decltype(range_tag)::value;    // blocks of the register range possible
+    constexpr bool LOADER = decltype(loader_tag)::value;  // one of the NLD loader waves
     if ((bi & (kWave - 1)) == 0) {
       const int jj = j_begin + bi + l;
       bool e = false;
@@ -366,12 +369,12 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       }
       ev = __builtin_amdgcn_ballot_w64(e);
     }
-    if (w < NLD) {  // the loaders' pieces of block bi have landed (block bi + 1 may be in flight)
+    if (LOADER) {  // the loaders' pieces of block bi have landed (block bi + 1 may be in flight)
       if (bi + 1 < nblk) wait_vmcnt<4>();
       else wait_vmcnt<0>();
     }
     barrier_keep_loads();  // block bi in LDS; every wave is done with block bi - 2
-    if (bi + 2 < nblk) issue(j_begin + bi + 2, (bi + 2) & 3);
+    if (LOADER && bi + 2 < nblk) issue(j_begin + bi + 2, (bi + 2) & 3);
     const int j = j_begin + bi;
     const unsigned char* stage = ring + (size_t)(bi & 3) * STAGE;
 
@@ -483,7 +486,9 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     }
 
       // ---- this wave's item of the block (at most one: items <= NW)
-      if ((ev >> (bi & (kWave - 1))) & 1ull) {
+      const bool has_item = ev & 1ull;  // bit 0 is block bi (shifted once per period)
+      ev >>= 1;
+      if (has_item) {
         const unsigned long long mm = masks[j];
         const unsigned long long m =
             ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(mm >> 32)) << 32) |
@@ -529,8 +534,13 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   };
   const int split = jr_hi >= jr_lo ? min(max(jr_lo - j_begin, 0), nblk) : nblk;
   int bi = 0;
-  for (; bi < split; ++bi) period(bi, RangeTag<false>{});
-  for (; bi < nblk; ++bi) period(bi, RangeTag<true>{});
+  if (w < NLD) {
+    for (; bi < split; ++bi) period(bi, RangeTag<false>{}, RangeTag<true>{});
+    for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, RangeTag<true>{});
+  } else {
+    for (; bi < split; ++bi) period(bi, RangeTag<false>{}, RangeTag<false>{});
+    for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, RangeTag<false>{});
+  }
   // the last block's items: after every wave has finished the previous
   // block's updates
   barrier_keep_loads();
