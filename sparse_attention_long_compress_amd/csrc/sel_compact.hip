@@ -323,7 +323,8 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // (the first two blocks were issued at the start of the kernel)
 
   // the wave's deferred item: P^T fragments, row, column validity, row sum
-  bool pend = false, dv = false;
+  int pend = 0;  // wave-uniform: this wave has a deferred item (an int, so it stays a scalar)
+  int dv = 0;  // per lane: the deferred item's column is a real row (an int, kept in a VGPR)
   FragT dp[2];
   int dr = 0;
   float dl = 0.f;
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     // ---- the deferred item of the previous block: P V, accumulator update
     if (pend) {
       finish_item(ring + (size_t)((bi - 1) & 3) * STAGE);
-      pend = false;
+      pend = 0;
     }
 
     if (RANGE && j >= jr_lo && j <= jr_hi) {
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     }
 
       // ---- this wave's item of the block (at most one: items <= NW)
-      const bool has_item = ev & 1ull;  // bit 0 is block bi (shifted once per period)
+      const bool has_item = (unsigned)ev & 1u;  // bit 0 is block bi (shifted once per period)
       ev >>= 1;
       if (has_item) {
         const unsigned long long mm = masks[j];
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         const int slot2pos = __builtin_amdgcn_ds_permute((bit ? rank : 63) * 4, l);
         const int slot = it * NSG + sg;
         const int pos = __builtin_amdgcn_ds_bpermute((slot & 63) * 4, slot2pos);
-        dv = slot < npos;
+        dv = slot < npos ? 1 : 0;
         dr = dv ? G * pos + hh : hh;         // unused columns read rows 0 .. 3 (finite)
         const float m1 = dv ? mref[dr] : INF;  // reference +inf: probability 0
         FragT qa[KS];
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
           dp[hf] = Frag<T>::from_f32(pv);
         }
         dl = xsum4(frag_sum(dp[0]) + frag_sum(dp[1]));
-        pend = true;
+        pend = 1;
       }
   };
   const int split = jr_hi >= jr_lo ? min(max(jr_lo - j_begin, 0), nblk) : nblk;
