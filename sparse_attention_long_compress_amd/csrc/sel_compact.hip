@@ -358,18 +358,19 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // body without the register-range part (scalar issue, shared by the
   // 15 waves of a CU, bounds the walk); each period has one barrier on
   // either path, so every wave meets the same barriers.
+  // the item mask of blocks bi .. bi + 63 (bi a multiple of 64)
+  auto refresh = [&](int bi) __attribute__((always_inline)) {
+    const int jj = j_begin + bi + l;
+    bool e = false;
+    if (need_sel && jj <= c_last) {
+      const int d = deal[jj];
+      e = (w - (d & 15) + NW) % NW < (d >> 4);
+    }
+    ev = __builtin_amdgcn_ballot_w64(e);
+  };
   auto period = [&](int bi, auto range_tag, auto loader_tag) __attribute__((always_inline)) {
     constexpr bool RANGE = decltype(range_tag)::value;    // blocks of the register range possible
     constexpr bool LOADER = decltype(loader_tag)::value;  // one of the NLD loader waves
-    if ((bi & (kWave - 1)) == 0) {
-      const int jj = j_begin + bi + l;
-      bool e = false;
-      if (need_sel && jj <= c_last) {
-        const int d = deal[jj];
-        e = (w - (d & 15) + NW) % NW < (d >> 4);
-      }
-      ev = __builtin_amdgcn_ballot_w64(e);
-    }
     if (LOADER) {  // the loaders' pieces of block bi have landed (block bi + 1 may be in flight)
       if (bi + 1 < nblk) wait_vmcnt<4>();
       else wait_vmcnt<0>();
@@ -534,13 +535,31 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       }
   };
   const int split = jr_hi >= jr_lo ? min(max(jr_lo - j_begin, 0), nblk) : nblk;
+  // the periods in runs that end at multiples of 64: the item mask is
+  // refreshed at the start of each 64 blocks, not tested every period
   int bi = 0;
   if (w < NLD) {
-    for (; bi < split; ++bi) period(bi, RangeTag<false>{}, RangeTag<true>{});
-    for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, RangeTag<true>{});
+    while (bi < split) {
+      if ((bi & (kWave - 1)) == 0) refresh(bi);
+      const int stop = min(split, (bi | (kWave - 1)) + 1);
+      for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, RangeTag<true>{});
+    }
+    while (bi < nblk) {
+      if ((bi & (kWave - 1)) == 0) refresh(bi);
+      const int stop = min(nblk, (bi | (kWave - 1)) + 1);
+      for (; bi < stop; ++bi) period(bi, RangeTag<true>{}, RangeTag<true>{});
+    }
   } else {
-    for (; bi < split; ++bi) period(bi, RangeTag<false>{}, RangeTag<false>{});
-    for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, RangeTag<false>{});
+    while (bi < split) {
+      if ((bi & (kWave - 1)) == 0) refresh(bi);
+      const int stop = min(split, (bi | (kWave - 1)) + 1);
+      for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, RangeTag<false>{});
+    }
+    while (bi < nblk) {
+      if ((bi & (kWave - 1)) == 0) refresh(bi);
+      const int stop = min(nblk, (bi | (kWave - 1)) + 1);
+      for (; bi < stop; ++bi) period(bi, RangeTag<true>{}, RangeTag<false>{});
+    }
   }
   // the last block's items: after every wave has finished the previous
   // block's updates
