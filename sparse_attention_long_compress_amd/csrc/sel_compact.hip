@@ -154,6 +154,16 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // are in flight behind the setup's own global loads).
   if (nblk > 0) issue(j_begin, 0);
   if (nblk > 1) issue(j_begin + 1, 1);
+  // the walk's copies of blocks j_begin + 2, + 3, ... (loader waves): the
+  // lane's source address advances by one block image per call
+  const unsigned char* src_next = img_b + (size_t)(j_begin + 2) * STAGE + (size_t)w * 4096 + 16 * l;
+  auto issue_next = [&](int bf) __attribute__((always_inline)) {
+    unsigned char* stage = ring + (size_t)bf * STAGE + (size_t)w * 4096;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2)
+      __builtin_amdgcn_global_load_lds((const void*)(src_next + q2 * 1024), (void*)(stage + q2 * 1024), 16, 0, 0);
+    src_next += STAGE;
+  };
 
 
   // ------------------------------------------------------------ setup
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       else wait_vmcnt<0>();
     }
     barrier_keep_loads();  // block bi in LDS; every wave is done with block bi - 2
-    if (LOADER && bi + 2 < nblk) issue(j_begin + bi + 2, (bi + 2) & 3);
+    if (LOADER && bi + 2 < nblk) issue_next((bi + 2) & 3);
     const int j = j_begin + bi;
     const unsigned char* stage = ring + (size_t)(bi & 3) * STAGE;
 
@@ -386,12 +396,13 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       pend = 0;
     }
 
-    if (RANGE && j >= jr_lo && j <= jr_hi) {
-      // register range of the wave's own column group
-      const bool act_w = j >= jw_lo && j <= jw_hi;
-      const bool inr = j >= jr_lo && j <= jr_hi;
-      const bool sl = inr && valid && ((sb >> (j - jr_lo)) & 1u);
-      const bool act_s = inr && __builtin_amdgcn_ballot_w64(sl) != 0;
+    // (the second loop of the walk starts at the register range: j >= jr_lo)
+    if (RANGE && j <= jr_hi) {
+      // register range of the wave's own column group; when the window is
+      // on, the register range is exactly the window's blocks
+      const bool act_w = win_on;
+      const bool sl = valid && ((sb >> (j - jr_lo)) & 1u);
+      const bool act_s = __builtin_amdgcn_ballot_w64(sl) != 0;
       const bool wl = act_w && valid && j * kBlock <= tpos && j * kBlock + kBlock - 1 > tpos - W;
       const bool wlow = act_w && j <= jw_edge;
       const bool act0 = act_s || act_w;
