@@ -184,32 +184,37 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
     wait_vmcnt<0>();       // this wave's loads of group gi (the only ones in flight)
     barrier_keep_loads();  // all of group gi is in LDS; group gi-1's slots are free
     if (gi + 1 < ngrp) issue_group(gi + 1);
-    for (int qq = 0; qq < GB; ++qq) {
-      const int r = gi * GB + qq;
-      if (r >= nblk) break;
-      const int j = j_begin + r;
-      // does this column group attend block j, and does it need the element mask
-      bool act, masked;
+    // the group's blocks this column group attends, visited directly (the
+    // scalar tests of blocks it skips cost issue slots every wave pays):
+    // selection -- from one selected block of its rows to the next;
+    // window / compression -- the group's part of a contiguous range
+    const int jg0 = j_begin + gi * GB, jg1 = min(jg0 + GB, j_begin + nblk);
+    int jl = jg0, jh = jg1;
+    if constexpr (MODE == DQ_WIN) {
+      jl = max(jg0, jw_lo);
+      jh = nvf > 0 ? min(jg1, own + 1) : jl;
+    } else if constexpr (MODE == DQ_CMP) {
+      jh = nvf > 0 ? min(jg1, (nvis_l + kBlock - 1) / kBlock) : jl;
+    }
+    for (int j = MODE == DQ_SEL ? nsel : jl; j < (MODE == DQ_SEL ? jg1 : jh);
+         j = MODE == DQ_SEL ? nsel : j + 1) {
+      const int qq = j - jg0;
+      // does the block need the element mask; the row's reference
+      bool masked;
       float lr;
       if constexpr (MODE == DQ_SEL) {
-        act = j == nsel;
-        if (!act) continue;
         const bool sl = nxt == j;
         if (sl) {
           ++ptr;
           nxt = ptr < topk ? lists[p * topk + ptr] : 0x7fff;
         }
-        nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));
+        nsel = __builtin_amdgcn_readfirstlane(row_min16(nxt));  // > j: the lists ascend
         masked = j == own;
         lr = sl ? lse2 : INF;
       } else if constexpr (MODE == DQ_WIN) {
-        act = nvf > 0 && j >= jw_lo && j <= own;
-        if (!act) continue;
         masked = j == own || j <= jw_edge;
         lr = lse2;
       } else {
-        act = nvf > 0 && j * kBlock < nvis_l;
-        if (!act) continue;
         masked = j * kBlock + kBlock > nvis_f;
         lr = lse2;
       }
