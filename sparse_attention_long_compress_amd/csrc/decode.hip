@@ -529,8 +529,6 @@ __global__ __launch_bounds__((DecCfg<T, D>::NT)) void decode_kernel(Shape s, Dec
 namespace {
 template <int D>
 struct DecM {
-  static constexpr int NW = D == 64 ? 8 : 4;
-  static constexpr int NT = NW * kWave;
   static constexpr int KS = D / 32;       // k steps of Q K
   static constexpr int MT = D / 16;       // channel tiles of P V
   static constexpr int VST = kBlock + 8;  // elements per channel row of a V^T tile
@@ -559,6 +557,17 @@ __host__ __device__ inline DecMLds dec_mfma_lds(int G, int D, int NW, int ncap) 
   return o;
 }
 
+// Waves per workgroup of the bf16 kernel.  Head dim 64: eight (wave 0 on the
+// compressed scores, seven on the window's up to nine blocks).  Head dim 128:
+// six when their V^T tiles and the per-cache score arrays fit in 160 KB of
+// LDS, else four; six walk the window in two rounds instead of three
+// (4 -> 6 waves: 44.0 -> 42.2 us per step at 64 sequences x 8192, Hkv 4, G 4;
+// 10, 12 or 16 waves at head dim 64 were slower than 8).
+inline int dec_mfma_waves(int G, int D, int ncap) {
+  if (D == 64) return 8;
+  return dec_mfma_lds(G, D, 6, ncap).total_floats * 4 <= 160 * 1024 ? 6 : 4;
+}
+
 // row of score tile u (0..3) at tile row i (0..15) -> key within the block
 __device__ __forceinline__ int dkey(int u, int i) {
   return 32 * (u >> 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
@@ -578,10 +587,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 }  // namespace
 
-template <int D, int G>
-__global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, DecodeArgs a) {
+template <int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(Shape s, DecodeArgs a) {
   typedef bf16 T;
-  constexpr int NW = DecM<D>::NW, NT = DecM<D>::NT, KS = DecM<D>::KS, MT = DecM<D>::MT;
+  constexpr int NT = NW * kWave, KS = DecM<D>::KS, MT = DecM<D>::MT;
   constexpr int VST = DecM<D>::VST, VQ = DecM<D>::VQ;
   static_assert(G <= 16, "the heads of a group fill at most one 16-column tile");
   const float NINF = -__builtin_inff();
@@ -917,8 +926,7 @@ __global__ __launch_bounds__(DecM<D>::NT) void decode_mfma_kernel(Shape s, Decod
 size_t decode_lds_bytes(bool is_bf16, const Shape& s) {
   const int ncap = s.T / kBlock;
   if (is_bf16) {
-    const int NW = s.D == 64 ? DecM<64>::NW : DecM<128>::NW;
-    return (size_t)dec_mfma_lds(s.G, s.D, NW, ncap).total_floats * 4;
+    return (size_t)dec_mfma_lds(s.G, s.D, dec_mfma_waves(s.G, s.D, ncap), ncap).total_floats * 4;
   }
   const int wmax = (s.W - 1) / kBlock + 2 < ncap ? (s.W - 1) / kBlock + 2 : ncap;
   const int es = is_bf16 ? 2 : 4;
@@ -938,16 +946,26 @@ static hipError_t launch_dec(const Shape& s, const DecodeArgs& a, hipStream_t st
   return hipGetLastError();
 }
 
-template <int D, int G>
-static hipError_t launch_dec_mfma(const Shape& s, const DecodeArgs& a, hipStream_t st) {
+template <int D, int G, int NW>
+static hipError_t launch_dec_mfma_nw(const Shape& s, const DecodeArgs& a, hipStream_t st) {
   const size_t lds = decode_lds_bytes(true, s);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<D, G>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<D, G, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(s.B * s.Hkv), dim3(DecM<D>::NT), lds, st, s, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, NW>), dim3(s.B * s.Hkv), dim3(NW * kWave), lds, st, s, a);
   return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_dec_mfma(const Shape& s, const DecodeArgs& a, hipStream_t st) {
+  if constexpr (D == 64) {
+    return launch_dec_mfma_nw<D, G, 8>(s, a, st);
+  } else {
+    if (dec_mfma_waves(G, D, s.T / kBlock) == 6) return launch_dec_mfma_nw<D, G, 6>(s, a, st);
+    return launch_dec_mfma_nw<D, G, 4>(s, a, st);
+  }
 }
 
 template <int D>
