@@ -106,6 +106,11 @@ CASES = [
     # 126, 254, 510 and 1022)
     (W340, 3, 32768, [8000, 16000, 32768]),
     (W340.with_(top_k=8), 1, 65536, [65536]),
+    # head_dim 128 at long caches: six waves per workgroup (G = 4), and the
+    # four-wave form that G = 16 falls back to when its scores leave too
+    # little LDS for six V^T tiles
+    (W13, 2, 32768, [20000, 32768]),
+    (WMQA, 1, 65536, [65536]),
 ]
 
 
