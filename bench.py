@@ -1,7 +1,7 @@
 """Throughput benchmark of the MI355X NSA forward (one GPU).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                [--no-cpu-baseline] [--profile-only]
+                [--no-cpu-baseline] [--profile-only] [--no-extra]
 
 A step is one whole forward pass (pool, compressed attention + top-k,
 selection + window + gated combine) over one batch of seeded synthetic input
@@ -13,8 +13,14 @@ Prints ONE JSON line (rank 0, N = 1):
                attention FLOPs per launch / its average duration, measured with
                HIP events recorded around it on its own stream in every timed
                step, against the bf16 dense MFMA peak
-  cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
-               same workload (query rows spread evenly over the sequence)
+  cpu_baseline = the fp64 oracle timed on the host (every core this process
+               may use; nproc and CPU model stated) on a bounded sample of the
+               same workload: whole forward passes, about ten seconds of them
+  workloads  = nested results (same fields) of the other seq-8192 and
+               long-context shapes: the 1.3B layer (B4 T8192 Hq16 Hkv4 D128),
+               the MQA ablation (B4 T8192 Hq16 Hkv1 D128: all branches, the
+               compression output pruned, the window alone) and the 32k layer
+               (B1 T32768 Hq16 Hkv4 D128, forward plus selection backward)
 """
 from __future__ import annotations
 
@@ -85,21 +91,31 @@ def algorithmic_bytes(wl):
     return es * (B * T * Hq * D * 2 + 2 * B * T * Hkv * D + B * T * Hq * 3)
 
 
-def oracle_threads():
-    """Host threads for the oracle: the cores this process may run on, at most 16."""
+def host_cores():
+    """Cores this process may run on (the host's CPU share)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return int(os.environ.get("NSA_ORACLE_THREADS", "0")) or max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, arrs_f64, min_seconds=10.0, max_passes=50):
-    """The fp64 oracle on the host: whole forward passes of the same workload,
-    repeated until at least min_seconds of CPU time have been measured."""
+    """The fp64 oracle on the host, on every core this process may use: whole
+    forward passes of the same workload, repeated until at least min_seconds
+    of wall time have been measured."""
     import oracle
 
-    threads = oracle_threads()
+    threads = int(os.environ.get("NSA_ORACLE_THREADS", "0")) or host_cores()
     passes, t_total = 0, 0.0
     while passes < max_passes and (passes == 0 or t_total < min_seconds):
         t0 = time.perf_counter()
@@ -109,7 +125,7 @@ def cpu_baseline(wl, arrs_f64, min_seconds=10.0, max_passes=50):
         passes += 1
     tokens = wl.batch * wl.seq_len
     return {"value": round(tokens * passes / t_total, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{passes} full forward pass(es) of {wl.name} (batch {wl.batch} x "
                       f"{wl.seq_len} positions, all heads, fp64), {t_total:.1f} s total"}
 
@@ -122,18 +138,18 @@ K3_SOURCES = ["sparse_attention_long_compress_amd/csrc/sel_win.hip",
               "sparse_attention_long_compress_amd/csrc/nsa_launch.h"]
 
 
-def k3_kernel(wl):
-    """Name of the selection/window kernel the library runs for this workload:
-    the packed-selection kernel covers bf16, head_dim 64, four query heads per
-    KV group, a window of at most 30 blocks and its LDS budget (sequences up to
-    8832); every other shape runs the general kernel."""
-    G = wl.n_q_heads // wl.n_kv_heads
-    nb = -(-wl.seq_len // 64)
-    lds = 159856 + 8 * nb
-    if (wl.dtype == "bf16" and wl.head_dim == 64 and G == 4 and (wl.window - 1) // 64 + 2 <= 32
-            and lds <= 160 * 1024):
-        return "sel_compact_kernel"
-    return "sel_win_kernel"
+def k3_kernel(wl, branches="all"):
+    """Name of the selection/window kernel the library runs for this workload
+    (asked from the library itself: nsa_forward_kernel)."""
+    import sparse_attention_long_compress_amd as nsa
+
+    flags = {"all": 0, "no-cmp": nsa.SKIP_CMP_OUT,
+             "window": nsa.SKIP_CMP_OUT | nsa.SKIP_SEL}[branches]
+    p = nsa.make_params(wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                        top_k=wl.top_k, window=wl.window,
+                        dtype=nsa.NSA_BF16 if wl.dtype == "bf16" else nsa.NSA_FP32,
+                        scale=wl.scale, flags=flags)
+    return nsa.forward_kernel(p)
 
 
 def kernel_source_hash(paths=K3_SOURCES):
@@ -264,6 +280,149 @@ def decode_bench(nsa, torch, np, wl, steps, warmup, batch=64):
                          "algorithmic_bytes": int(nbytes)}}
 
 
+def prepare(wl, with_dout):
+    """Seeded synthetic inputs of the workload, rounded once to its dtype,
+    resident in HBM (plus the rounded CPU copy for the oracle)."""
+    import torch
+
+    from sparse_attention_long_compress_amd.synth import draw, to_dtype
+
+    arrs = draw(wl, with_dout=with_dout)
+    cpu = to_dtype(arrs, wl.dtype)
+    dev = {k: v.to("cuda") for k, v in cpu.items()}
+    torch.cuda.synchronize()
+    return dev, cpu
+
+
+def time_forward(nsa, torch, np, wl, dev, steps, warmup, branches="all"):
+    """Forward steps of the workload timed with the host clock (bracketed by
+    synchronisations) and per kernel with HIP events recorded by the library
+    around each of its three kernels on the launch stream."""
+    bflags = {"all": 0, "no-cmp": nsa.SKIP_CMP_OUT,
+              "window": nsa.SKIP_CMP_OUT | nsa.SKIP_SEL}[branches]
+    p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale,
+                       flags=bflags)
+    ws = nsa.alloc_workspace(p, dev["q"].device)
+    out = torch.empty_like(dev["q"])
+
+    def step(events=None):
+        nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                    window=wl.window, scale=wl.scale, out=out, workspace=ws, events=events,
+                    flags=bflags)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # events (created by torch on the current stream's device; raw handles go to the library)
+    evs = []
+    for _ in range(steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in row:
+            e.record()  # materialise the underlying hipEvent_t
+        evs.append(row)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events=[e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
+    k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
+    k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
+    ev_step = np.mean([r[0].elapsed_time(r[3]) for r in evs]) * 1e-3
+    fl = useful_flops(wl, branches)
+    tokens = wl.batch * wl.seq_len
+    achieved = fl["sel_win"] / k3 / 1e12
+    kern = k3_kernel(wl, branches)
+    return {
+        "wall": wall, "ws": ws,
+        "tokens_per_s": round(tokens / wall, 1),
+        "ms_per_step": round(wall * 1e3, 4),
+        "useful_tflops": round(fl["total"] / wall / 1e12, 2),
+        "pct_bf16_peak": round(100 * fl["total"] / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "stage_us": {"pool": round(k1 * 1e6, 2), "cmp_select": round(k2 * 1e6, 2),
+                     "sel_win_combine": round(k3 * 1e6, 2), "events_total": round(ev_step * 1e6, 2)},
+        "roofline": {"kernel": kern, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": committed_traffic(wl.name, kern) if branches == "all" else None},
+    }
+
+
+def time_select_bwd(nsa, torch, np, wl, dev, ws, steps, warmup):
+    """The selection-branch backward of the same input, fed by the forward's
+    saved indices, log-sum-exp and o_sel; HIP events around each call."""
+    p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale)
+    res_f = nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                        window=wl.window, scale=wl.scale, workspace=ws, want_indices=True,
+                        want_lse=True, want_o_sel=True)
+    wsb = nsa.alloc_workspace(p, dev["q"].device, backward=True)
+    grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]))
+
+    def bstep():
+        nsa.select_bwd(dev["q"], dev["k"], dev["v"], dev["gates"], res_f["indices"],
+                       res_f["lse_sel"], res_f["o_sel"], dev["dout"], top_k=wl.top_k,
+                       scale=wl.scale, workspace=wsb, out=grads)
+
+    for _ in range(warmup):
+        bstep()
+    torch.cuda.synchronize()
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in bev:
+        e0.record()
+        bstep()
+        e1.record()
+    torch.cuda.synchronize()
+    bwd = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])) * 1e-3
+    fb = useful_bwd_flops(wl)
+    return bwd, {"us": round(bwd * 1e6, 2), "useful_tflops": round(fb / bwd / 1e12, 2),
+                 "pct_bf16_peak": round(100 * fb / bwd / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
+def public(d):
+    return {k: v for k, v in d.items() if k not in ("wall", "ws")}
+
+
+def extra_configs(nsa, torch, np, steps, warmup):
+    """The other seq-8192 / long-context workloads, each a nested result:
+    1.3B (B4 T8192 Hq16 Hkv4 D128) forward; the MQA ablation (B4 T8192 Hq16
+    Hkv1 D128) with all branches, the compression output pruned, and the
+    window alone; the 32k forward plus selection backward (B1 T32768 Hq16
+    Hkv4 D128)."""
+    from sparse_attention_long_compress_amd.synth import WORKLOADS
+
+    out = {}
+    wl = WORKLOADS["1b3-gqa4"]
+    print(f"# timing {wl.name}", file=sys.stderr, flush=True)
+    dev, _ = prepare(wl, False)
+    out[wl.name] = public(time_forward(nsa, torch, np, wl, dev, steps, warmup))
+    del dev
+    torch.cuda.empty_cache()
+    wl = WORKLOADS["mqa-ablation"]
+    print(f"# timing {wl.name}", file=sys.stderr, flush=True)
+    dev, _ = prepare(wl, False)
+    runs = {}
+    for br in ("all", "no-cmp", "window"):
+        runs[br] = public(time_forward(nsa, torch, np, wl, dev, steps, warmup, br))
+    runs["window_only_speedup"] = round(runs["all"]["ms_per_step"] / runs["window"]["ms_per_step"], 2)
+    out[wl.name] = runs
+    del dev
+    torch.cuda.empty_cache()
+    wl = WORKLOADS["32k-fwd-bwd"]
+    print(f"# timing {wl.name}", file=sys.stderr, flush=True)
+    dev, _ = prepare(wl, True)
+    f = time_forward(nsa, torch, np, wl, dev, steps, warmup)
+    bwd, b = time_select_bwd(nsa, torch, np, wl, dev, f["ws"], steps, warmup)
+    r = public(f)
+    r["selection_backward"] = b
+    r["fwd_plus_bwd_tokens_per_s"] = round(wl.batch * wl.seq_len / (f["wall"] + bwd), 1)
+    out[wl.name] = r
+    del dev, f
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +453,8 @@ def main():
                     help="time the forward only (the selection-branch backward and a training "
                          "step -- forward with saved tensors plus the full backward -- are timed "
                          "by default)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the nested results of the 1.3B, MQA-ablation and 32k workloads")
     args = ap.parse_args()
     if args.pmc_summary:
         from sparse_attention_long_compress_amd.synth import WORKLOADS as _W
@@ -313,22 +474,20 @@ def main():
     import torch
 
     import sparse_attention_long_compress_amd as nsa
-    from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64, draw, to_dtype
+    from sparse_attention_long_compress_amd.synth import WORKLOADS, as_f64
 
     wl = WORKLOADS[args.workload]
     if args.branches != "all":
         args.no_backward = True
         args.no_decode = True
-    bflags = {"all": 0, "no-cmp": nsa.SKIP_CMP_OUT, "window": nsa.SKIP_CMP_OUT | nsa.SKIP_SEL}[args.branches]
-    arrs = draw(wl, with_dout=not args.no_backward)
-    cpu = to_dtype(arrs, wl.dtype)
-    dev = {k: v.to("cuda") for k, v in cpu.items()}
-    del arrs
+        args.no_extra = True
+    if args.workload != "340m-gqa4" or args.profile_only or args.ab_single:
+        args.no_extra = True
+    dev, cpu = prepare(wl, not args.no_backward or args.ab_single)
     p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale)
-    ws = nsa.alloc_workspace(p, dev["q"].device)
-    out = torch.empty_like(dev["q"])
 
     if args.ab_single:
+        ws = nsa.alloc_workspace(p, dev["q"].device)
         res_f = nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
                             window=wl.window, scale=wl.scale, workspace=ws, want_indices=True,
                             want_lse=True, want_o_sel=True)
@@ -355,56 +514,13 @@ def main():
               flush=True)
         return
 
-    def step(events=None):
-        nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
-                    window=wl.window, scale=wl.scale, out=out, workspace=ws, events=events,
-                    flags=bflags)
+    fwd = time_forward(nsa, torch, np, wl, dev, args.steps, args.warmup, args.branches)
+    wall, ws = fwd["wall"], fwd["ws"]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # events (created by torch on the current stream's device; raw handles go to the library)
-    evs = []
-    for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for e in row:
-            e.record()  # materialise the underlying hipEvent_t
-        evs.append(row)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events=[e.cuda_event for e in evs[i]])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
-
-    # the rest of the hot path: the selection-branch backward of the same
-    # input, fed by the forward's saved indices, log-sum-exp and o_sel
-    bwd = None
+    # the rest of the hot path: the selection-branch backward of the same input
+    bwd = bres = None
     if not args.no_backward:
-        res_f = nsa.forward(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
-                            window=wl.window, scale=wl.scale, workspace=ws, want_indices=True,
-                            want_lse=True, want_o_sel=True)
-        wsb = nsa.alloc_workspace(p, dev["q"].device, backward=True)
-        grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]))
-
-        def bstep():
-            nsa.select_bwd(dev["q"], dev["k"], dev["v"], dev["gates"], res_f["indices"],
-                           res_f["lse_sel"], res_f["o_sel"], dev["dout"], top_k=wl.top_k,
-                           scale=wl.scale, workspace=wsb, out=grads)
-
-        for _ in range(args.warmup):
-            bstep()
-        torch.cuda.synchronize()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for e0, e1 in bev:
-            e0.record()
-            bstep()
-            e1.record()
-        torch.cuda.synchronize()
-        bwd = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])) * 1e-3
+        bwd, bres = time_select_bwd(nsa, torch, np, wl, dev, ws, args.steps, args.warmup)
 
     # a training step: the forward that saves every tensor the full backward
     # needs, then the gradient of all three branches and the gates
@@ -434,32 +550,29 @@ def main():
         tev = tev[args.warmup:]
         train = (float(np.mean([e[0].elapsed_time(e[1]) for e in tev])) * 1e-3,
                  float(np.mean([e[1].elapsed_time(e[2]) for e in tev])) * 1e-3)
+        del wsf, saved, fgrads
 
-    k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
-    k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
-    k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
-    ev_step = np.mean([r[0].elapsed_time(r[3]) for r in evs]) * 1e-3
-    fl = useful_flops(wl, args.branches)
     tokens = wl.batch * wl.seq_len
     if args.profile_only:
         dec = None if args.no_decode else decode_bench(nsa, torch, np, wl, args.steps, args.warmup)
+        st = fwd["stage_us"]
         print(json.dumps({"profile_only": True, "ms_per_step": wall * 1e3,
                           "decode_us": None if dec is None else dec["step_us"],
-                          "k1_us": k1 * 1e6, "k2_us": k2 * 1e6, "k3_us": k3 * 1e6,
+                          "k1_us": st["pool"], "k2_us": st["cmp_select"],
+                          "k3_us": st["sel_win_combine"],
                           "sel_bwd_us": None if bwd is None else bwd * 1e6,
                           "train_fwd_us": None if train is None else train[0] * 1e6,
                           "full_bwd_us": None if train is None else train[1] * 1e6}), flush=True)
         return
 
-    achieved = fl["sel_win"] / k3 / 1e12
     res = {
         "metric": METRIC,
-        "value": round(tokens / wall, 1),
+        "value": fwd["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3, 4),
+        "ms_per_step": fwd["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -469,24 +582,17 @@ def main():
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "block": 64, "top_k": wl.top_k,
                    "window": wl.window, "branches": args.branches, "parallelism": "none (1 GPU)"},
-        "useful_tflops": round(fl["total"] / wall / 1e12, 2),
-        "pct_bf16_peak": round(100 * fl["total"] / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "stage_us": {"pool": round(k1 * 1e6, 2), "cmp_select": round(k2 * 1e6, 2),
-                     "sel_win_combine": round(k3 * 1e6, 2), "events_total": round(ev_step * 1e6, 2)},
-        "roofline": {"kernel": k3_kernel(wl), "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": committed_traffic(wl.name, k3_kernel(wl))},
+        "useful_tflops": fwd["useful_tflops"],
+        "pct_bf16_peak": fwd["pct_bf16_peak"],
+        "stage_us": fwd["stage_us"],
+        "roofline": fwd["roofline"],
     }
     if bwd is not None:
-        fb = useful_bwd_flops(wl)
-        res["selection_backward"] = {
-            "us": round(bwd * 1e6, 2), "useful_tflops": round(fb / bwd / 1e12, 2),
-            "pct_bf16_peak": round(100 * fb / bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "fwd_plus_bwd_ms": round((wall + bwd) * 1e3, 4),
-            "fwd_plus_bwd_tokens_per_s": round(tokens / (wall + bwd), 1)}
+        bres["fwd_plus_bwd_ms"] = round((wall + bwd) * 1e3, 4)
+        bres["fwd_plus_bwd_tokens_per_s"] = round(tokens / (wall + bwd), 1)
+        res["selection_backward"] = bres
     if train is not None:
-        ff, fbf = fl["total"], useful_full_bwd_flops(wl)
+        ff, fbf = useful_flops(wl)["total"], useful_full_bwd_flops(wl)
         step_s = train[0] + train[1]
         res["training_step"] = {
             "forward_us": round(train[0] * 1e6, 2), "full_backward_us": round(train[1] * 1e6, 2),
@@ -495,6 +601,10 @@ def main():
             "pct_bf16_peak": round(100 * (ff + fbf) / step_s / 1e12 / PEAK_BF16_TFLOPS, 2)}
     if not args.no_decode:
         res["decode"] = decode_bench(nsa, torch, np, wl, args.steps, args.warmup)
+    del fwd, ws, dev
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["workloads"] = extra_configs(nsa, torch, np, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         f64 = {k: as_f64(v) for k, v in cpu.items()}
         res["cpu_baseline"] = cpu_baseline(wl, f64)

@@ -138,6 +138,12 @@ nsa_status_t nsa_compress_select(const void* q, const void* k, const void* v,
                                  const nsa_params_t* p, void* o_cmp, int32_t* indices,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/* Name of the selection / window / combine kernel that nsa_forward launches
+ * for these params (a static string: "sel_compact_kernel" or
+ * "sel_win_kernel"), or NULL when nsa_check_params rejects them.  Touches no
+ * device; for measurement tools that attribute kernel time. */
+const char* nsa_forward_kernel(const nsa_params_t* p);
+
 /* Full NSA forward (all three branches and the gated combination).
  *   out      : required, [B][T][Hq][D] in params->dtype.
  *   indices  : nullable output (or required input with NSA_INDICES_IN).

@@ -20,13 +20,20 @@ Parity-pin status (what pins each function; see tests/test_oracle_pins.py):
                     "Sparsity is Cool" Key claims (tests/golden)
   forward/o_sel     full causal attention when top-k covers all blocks (torch
                     SDPA), explicit-mask SDPA given the index table
+  forward/lse_cmp   torch logsumexp over avg-pooled keys with the block-causal
+                    mask; constant keys give tau q.c + log n_c (closed form)
+  forward/lse_sel   torch logsumexp of causal attention (full coverage) and of
+                    the explicit mask given the index table
   forward/o_win     W >= T full causal, W = 1 returns v_t, banded-mask SDPA
+  forward/lse_win   torch logsumexp over the band; W >= T gives the causal
+                    log-sum-exp, W = 1 gives tau q_t.k_t (closed forms)
   forward/out       zero gates, unit gates, linearity, shift invariances
   select_bwd        central finite differences, torch autograd of causal and
                     masked SDPA
   decode            the forward restricted to the last row of each prefix (its
                     definition); pinned by an explicit per-query enumeration of
-                    the compressed, selected and window key sets in the tests
+                    the compressed, selected and window key sets in the tests;
+                    its importance scores are those of forward/indices
 """
 from __future__ import annotations
 
@@ -221,14 +228,17 @@ def decode(q, k_cache, v_cache, gates, seq_lens, *, top_k: int, window: int, blk
     t = L - 1, and its output is the prefill output of row t over the first L
     positions.  q [B,Hq,D], k_cache/v_cache [B,Lmax,Hkv,D], gates [B,Hq,3].
     ``indices`` (optional int32 [B,Hkv,top_k]) freezes the selection.
-    Returns out, o_cmp, o_sel, o_win [B,Hq,D], indices [B,Hkv,top_k] and the
-    k-th vs (k+1)-th importance gap [B,Hkv]."""
+    Returns out, o_cmp, o_sel, o_win [B,Hq,D], indices [B,Hkv,top_k], the
+    k-th vs (k+1)-th importance gap [B,Hkv] and the block importance scores
+    [B,Hkv,ceil(Lmax/blk)] of each sequence's query row (0 past its complete
+    blocks)."""
     q, kc, vc, gates = _f64(q), _f64(k_cache), _f64(v_cache), _f64(gates)
     B, Hq, D = q.shape
     Hkv = kc.shape[2]
     res = {n: np.zeros((B, Hq, D)) for n in ("out", "o_cmp", "o_sel", "o_win")}
     res["indices"] = np.zeros((B, Hkv, top_k), dtype=np.int32)
     res["gap"] = np.zeros((B, Hkv))
+    res["scores"] = np.zeros((B, Hkv, -(-kc.shape[1] // blk)))
     for b in range(B):
         L = int(seq_lens[b])
         t = L - 1
@@ -241,9 +251,12 @@ def decode(q, k_cache, v_cache, gates, seq_lens, *, top_k: int, window: int, blk
             idx = np.zeros((1, Hkv, L, top_k), dtype=np.int32)
             idx[0, :, t] = np.asarray(indices)[b]
         r = forward(qf, kc[b:b + 1, :L], vc[b:b + 1, :L], gf, top_k=top_k, window=window,
-                    blk=blk, scale=scale, indices=idx, rows=[t], threads=threads)
+                    blk=blk, scale=scale, indices=idx, rows=[t], want_scores=True,
+                    threads=threads)
         for n in ("out", "o_cmp", "o_sel", "o_win"):
             res[n][b] = r[n][0, t]
         res["indices"][b] = r["indices"][0, :, t]
         res["gap"][b] = r["gap"][0, :, t]
+        sc = r["scores"][0, :, t]
+        res["scores"][b, :, :sc.shape[-1]] = sc
     return res

@@ -18,7 +18,8 @@ NSA_BF16, NSA_FP32 = 0, 1
 SKIP_CMP_OUT, SKIP_SEL, SKIP_WIN, INDICES_IN = 1, 2, 4, 8
 
 EXPORTED = (
-    "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_workspace_size",
+    "nsa_abi_version", "nsa_status_string", "nsa_check_params", "nsa_forward_kernel",
+    "nsa_workspace_size",
     "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
     "nsa_forward_train", "nsa_backward", "nsa_select_bwd_single", "nsa_decode",
 )
@@ -64,6 +65,8 @@ def lib():
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_check_params.argtypes = [P]
         L.nsa_check_params.restype = ctypes.c_int
+        L.nsa_forward_kernel.argtypes = [P]
+        L.nsa_forward_kernel.restype = ctypes.c_char_p
         L.nsa_workspace_size.argtypes = [P, ctypes.c_int]
         L.nsa_workspace_size.restype = ctypes.c_size_t
         L.nsa_pool.argtypes = [vp, vp, P, vp, vp, vp]
@@ -138,6 +141,15 @@ def params_for(q, k, *, top_k, window, scale=None, flags=0):
     Hkv = k.shape[2]
     return make_params(B, T, Hq, Hkv, D, top_k=top_k, window=window, dtype=_dtype_code(q),
                        scale=scale, flags=flags)
+
+
+def forward_kernel(p: NsaParams) -> str:
+    """Name of the selection/window/combine kernel nsa_forward runs for p
+    (nsa_forward_kernel)."""
+    name = lib().nsa_forward_kernel(ctypes.byref(p))
+    if name is None:
+        _check(lib().nsa_check_params(ctypes.byref(p)), "nsa_forward_kernel")
+    return name.decode()
 
 
 def workspace_size(p: NsaParams, backward=False) -> int:

@@ -151,6 +151,11 @@ const char* nsa_status_string(nsa_status_t st) {
 
 nsa_status_t nsa_check_params(const nsa_params_t* p) { return check(p); }
 
+const char* nsa_forward_kernel(const nsa_params_t* p) {
+  if (check(p) != NSA_OK) return nullptr;
+  return nsa::sel_win_kernel_name(p->dtype == NSA_BF16, make_shape(p));
+}
+
 size_t nsa_workspace_size(const nsa_params_t* p, int for_backward) {
   if (check(p) != NSA_OK) return 0;
   const Shape s = make_shape(p);

@@ -61,6 +61,8 @@ hipError_t launch_decode(bool is_bf16, const Shape& s, const void* q, const void
                          const int32_t* lens, const void* gates, void* out, int32_t* indices,
                          hipStream_t st);
 
+// name of the kernel launch_sel_win runs for this shape
+const char* sel_win_kernel_name(bool is_bf16, const Shape& s);
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,
                           const void* kvimg, const void* gates, const void* o_cmp,
                           const float* knorm, const int32_t* indices, void* out, float* lse,

@@ -429,11 +429,14 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
 
         FragT ps[2], pw[2];
         const bool diag = j == own;
-        const bool dual = exact && act_s && act_w;
+        // with exact references the window's maximum differs from the
+        // selection's: every block the window attends takes the
+        // two-reference path (also where no row selected the block)
+        const bool dual = exact && act_w;
         if (!diag && !wlow && !dual) {
           const bool both = act_s && act_w;
           const bool att = act_s ? sl : wl;
-          const float mr = (both ? (sl || wl) : att) ? mr_s : INF;  // mr_s == mr_w here
+          const float mr = (both ? (sl || wl) : att) ? mr_s : INF;  // mr_s == mr_w unless exact
           FragT pf[2];
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {

@@ -405,11 +405,13 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
       if (!act[cg]) continue;
       const int t = tpos[cg];
       const bool diag = j == own[cg];
-      const bool dual = exact && act_s[cg] && act_w[cg];  // two references only after the exact pass
+      // after the exact pass the two branches have different references:
+      // every block the window attends takes the two-reference path
+      const bool dual = exact && act_w[cg];
       if (!diag && !wlow[cg] && !dual) {
         const bool both = act_s[cg] && act_w[cg];
         const bool att = act_s[cg] ? sl[cg] : wl[cg];
-        const float mr = (both ? (sl[cg] || wl[cg]) : att) ? mr_s[cg] : INF;  // mr_s == mr_w here
+        const float mr = (both ? (sl[cg] || wl[cg]) : att) ? mr_s[cg] : INF;  // mr_s == mr_w unless exact
         FragT pf[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -544,6 +546,10 @@ static hipError_t launch_sw_g(const Shape& s, const SelWinArgs& a, hipStream_t s
     case 8: return launch_sw<T, D, 8>(s, a, st);
     default: return launch_sw<T, D, 16>(s, a, st);
   }
+}
+
+const char* sel_win_kernel_name(bool is_bf16, const Shape& s) {
+  return NSA_K3_COMPACT && sel_compact_eligible(is_bf16, s) ? "sel_compact_kernel" : "sel_win_kernel";
 }
 
 hipError_t launch_sel_win(bool is_bf16, const Shape& s, const void* q, const void* k,

@@ -66,6 +66,18 @@ def test_check_params(kw, code):
     assert nsa.lib().nsa_check_params(ctypes.byref(p)) == code
 
 
+def test_forward_kernel_names():
+    # bf16, head_dim 64, four heads per group, window within 32 blocks: the
+    # packed-selection kernel; everything else the general one; NULL if invalid
+    assert nsa.forward_kernel(params(T=8192, Hq=16, Hkv=4, top_k=16, window=512)) == "sel_compact_kernel"
+    assert nsa.forward_kernel(params(T=8192, Hq=16, Hkv=4, D=128, top_k=16, window=512)) == "sel_win_kernel"
+    assert nsa.forward_kernel(params(T=8192, Hq=16, Hkv=4, top_k=16, window=4096)) == "sel_win_kernel"
+    assert nsa.forward_kernel(params(dtype=nsa.NSA_FP32)) == "sel_win_kernel"
+    assert nsa.lib().nsa_forward_kernel(ctypes.byref(params(D=96))) is None
+    with pytest.raises(nsa.NsaError, match="UNSUPPORTED"):
+        nsa.forward_kernel(params(D=96))
+
+
 def test_check_params_null():
     assert nsa.lib().nsa_check_params(None) == ENULL
 

@@ -5,11 +5,14 @@ log-sum-exp and selection output that the backward consumes match the
 oracle's selection exactly.
 
 Tolerances: the pages give none for gradients.  Reading used here: the
-forward's bounds scaled by the gradient's own magnitude -- max-abs <= 2e-2 *
-max(1, max|ref|) and mean-abs <= 2e-3 * max(1, rms_ref) for bf16, 1e-4 *
-max(1, max|ref|) for fp32.  dk/dv are fp32 sums over thousands of (query,
-head) terms whose MFMA operands (P, g_sel dO) are rounded to bf16 once, so the
-worst element's error scales with the largest accumulated values, not with 1."""
+forward's bounds scaled by the gradient's root-mean-square magnitude --
+max-abs <= 2e-2 * max(1, rms_ref) and mean-abs <= 2e-3 * max(1, rms_ref) for
+bf16, 1e-4 * max(1, rms_ref) for fp32 -- with one addition for bf16: every
+product in a gradient sum has both operands rounded to bf16 once (P, dS and
+g_sel dO; unit roundoff 2^-8 each), so an element carries a relative error of
+up to 2^-7 of its own magnitude on top of that (its size is set by its own
+terms, e.g. the first keys, which few queries share, get gradients ~50x the
+rms).  Each case prints its measured errors."""
 import numpy as np
 import pytest
 import torch
@@ -22,17 +25,22 @@ from tests.nsa_cases import device_inputs, oracle_forward, to_np
 pytestmark = pytest.mark.gpu
 
 
+REL_BF16 = 2.0 ** -7
+
+
 def grad_close(got, ref, dtype, what):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     rms = max(1.0, float(np.sqrt((ref ** 2).mean())))
-    big = max(1.0, float(np.abs(ref).max()))
     err = np.abs(got - ref)
     mx, mean = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
-    print(f"{what}: max|ref| {big:.3g} rms_ref {rms:.3g} max-abs {err.max():.3e} "
-          f"mean-abs {err.mean():.3e}", flush=True)
-    assert err.max() <= mx * big, f"{what}: max-abs {err.max():.3e} > {mx * big:.3e}"
+    rel = REL_BF16 if dtype == "bf16" else 0.0
+    excess = float((err - rel * np.abs(ref)).max())
+    print(f"{what}: max|ref| {np.abs(ref).max():.3g} rms_ref {np.sqrt((ref ** 2).mean()):.3g} "
+          f"max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
+          f"max(|err| - {rel:.3g}|ref|) {excess:.3e} bound {mx * rms:.1e}", flush=True)
+    assert excess <= mx * rms, f"{what}: max(|err| - {rel}|ref|) {excess:.3e} > {mx * rms:.3e}"
     assert err.mean() <= mean * rms, f"{what}: mean-abs {err.mean():.3e} > {mean * rms:.3e}"
 
 
@@ -75,6 +83,15 @@ def test_select_bwd_matches_oracle(name, T, over):
     got, ref, *_ = run_both(wl, T)
     for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
         grad_close(to_np(g_), r_, wl.dtype, nm)
+
+
+def test_select_bwd_full_size_340m():
+    # the launch the bench times: 340M shapes at T = 8192, every element
+    wl = WORKLOADS["340m-gqa4"]
+    print("case 340m-gqa4 full size", flush=True)
+    got, ref, *_ = run_both(wl, wl.seq_len)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        grad_close(to_np(g_), r_, wl.dtype, nm + "@8192")
 
 
 def test_select_bwd_is_bitwise_reproducible():

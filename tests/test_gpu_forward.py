@@ -8,7 +8,7 @@ import oracle
 import sparse_attention_long_compress_amd as nsa
 from sparse_attention_long_compress_amd.synth import WORKLOADS, Workload
 from tests.nsa_cases import (assert_close, check_indices, device_inputs, gpu_forward,
-                             oracle_forward, rows_mask_from_groups, to_np)
+                             oracle_forward, to_np)
 
 # Saved log-sum-exp of the selection softmax.  The library normalises with the
 # sum of the bf16-rounded probabilities it feeds to the PV product (so that the
@@ -122,15 +122,16 @@ def test_forward_matches_oracle(name, T, planted, over):
     res = gpu_forward(wl, dev, want_indices=True, want_lse=True, want_o_sel=True)
     torch.cuda.synchronize()
     ora = oracle_forward(wl, f64, want_scores=True)
-    agree = check_indices(res["indices"].cpu().numpy(), ora, wl.top_k, scores=ora["scores"])
-    rows = rows_mask_from_groups(agree, wl.n_q_heads)
-    assert rows.mean() > 0.9
-    assert_close(to_np(res["out"])[rows], ora["out"][rows], wl.dtype, "out")
-    assert_close(to_np(res["o_sel"])[rows], ora["o_sel"][rows], wl.dtype, "o_sel")
-    lse_rows = np.transpose(rows, (0, 2, 1))
-    lse_tol = LSE_TOL[wl.dtype]
-    err = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"])[lse_rows]
-    assert err.max() < lse_tol, err.max()
+    gi = res["indices"].cpu().numpy()
+    agree = check_indices(gi, ora, wl.top_k, scores=ora["scores"])
+    _print("index agreement", agree.mean(), "decisive", (ora["gap"] > 1e-3).mean())
+    # every row, against the oracle on the GPU's index table (near-tie reading)
+    if not agree.all():
+        ora = oracle_forward(wl, f64, indices=gi)
+    assert_close(to_np(res["out"]), ora["out"], wl.dtype, "out")
+    assert_close(to_np(res["o_sel"]), ora["o_sel"], wl.dtype, "o_sel")
+    err = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"])
+    assert err.max() < LSE_TOL[wl.dtype], err.max()
 
 
 def test_forward_with_oracle_indices_every_row():
@@ -147,22 +148,40 @@ def test_forward_with_oracle_indices_every_row():
     assert torch.equal(idx.cpu(), torch.from_numpy(ora["indices"]))  # input left untouched
 
 
-def test_skip_flags_equal_zero_gates():
+def _skip_flag_case(wl, dev, f64, flag):
+    """GPU output with a skip flag against the oracle run on the gates with the
+    skipped branches' gates zeroed ("a zero gate removes its branch"); where the
+    selection branch contributes, the oracle takes the GPU's own index table
+    (near-ties may pick either valid set)."""
+    zero = [i for i, f in ((0, nsa.SKIP_CMP_OUT), (1, nsa.SKIP_SEL), (2, nsa.SKIP_WIN)) if flag & f]
+    sel_used = not (flag & nsa.SKIP_SEL)
+    res = gpu_forward(wl, dev, flags=flag, want_indices=sel_used)
+    torch.cuda.synchronize()
+    gz = f64["gates"].copy()
+    gz[..., zero] = 0.0
+    idx = res["indices"].cpu().numpy() if sel_used else None
+    ora = oracle.forward(f64["q"], f64["k"], f64["v"], gz, top_k=wl.top_k, window=wl.window,
+                         scale=wl.scale, indices=idx)
+    assert_close(to_np(res["out"]), ora["out"], wl.dtype, f"out (flags {flag})")
+
+
+@pytest.mark.parametrize("flag", [nsa.SKIP_CMP_OUT, nsa.SKIP_SEL, nsa.SKIP_WIN,
+                                  nsa.SKIP_CMP_OUT | nsa.SKIP_SEL])
+def test_skip_flags_match_oracle_with_zero_gates(flag):
     wl = WORKLOADS["340m-gqa4"]
-    dev, _ = device_inputs(wl, seq_len=1024, planted_sigma=1.0)
-    for flag, gi in ((nsa.SKIP_CMP_OUT, 0), (nsa.SKIP_SEL, 1), (nsa.SKIP_WIN, 2),
-                     (nsa.SKIP_CMP_OUT | nsa.SKIP_SEL, None)):
-        a = gpu_forward(wl, dev, flags=flag)["out"]
-        gz = dev["gates"].clone()
-        if gi is None:
-            gz[..., 0] = 0
-            gz[..., 1] = 0
-        else:
-            gz[..., gi] = 0
-        b = gpu_forward(wl, {**dev, "gates": gz})["out"]
-        torch.cuda.synchronize()
-        d = (a.double() - b.double()).abs().max().item()
-        assert d <= 1e-2, (flag, d)  # same sums up to accumulation order
+    _print("case skip flag", flag)
+    dev, f64 = device_inputs(wl, seq_len=2048)
+    _skip_flag_case(wl, dev, f64, flag)
+
+
+def test_mqa_ablation_runs_match_oracle():
+    # The MQA ablation at its full size (B4 T8192 Hq16 Hkv1 D128): all branches,
+    # compression output pruned (g_cmp = 0), window only (g_cmp = g_sel = 0).
+    wl = WORKLOADS["mqa-ablation"]
+    dev, f64 = device_inputs(wl)
+    for flag in (0, nsa.SKIP_CMP_OUT, nsa.SKIP_CMP_OUT | nsa.SKIP_SEL):
+        _print("case mqa ablation flags", flag)
+        _skip_flag_case(wl, dev, f64, flag)
 
 
 def test_window_only_matches_oracle():
@@ -176,40 +195,56 @@ def test_window_only_matches_oracle():
 
 def test_large_logits_take_the_exact_maximum_path():
     # q scaled x40: the logit bound minus the forced maximum exceeds the fixed
-    # reference window, so the kernel computes exact maxima over the free blocks.
+    # reference window, so the kernel computes exact maxima of both branches.
+    # At T = 2048 (32 blocks, top-k 16) window blocks that no row of a column
+    # group selected exist, so the window's own reference is exercised; every
+    # saved tensor of both branches is compared.
     wl = WORKLOADS["340m-gqa4"]
-    dev, f64 = device_inputs(wl, seq_len=1024, planted_sigma=1.0, q_scale=40.0)
+    dev, f64 = device_inputs(wl, seq_len=2048, planted_sigma=1.0, q_scale=40.0)
     ora = oracle_forward(wl, f64)
     idx = torch.from_numpy(ora["indices"]).to("cuda")
-    res = gpu_forward(wl, dev, indices=idx, want_o_sel=True, want_lse=True)
+    sv = nsa.forward_train(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                           window=wl.window, scale=wl.scale, indices=idx)
     torch.cuda.synchronize()
-    assert_close(to_np(res["o_sel"]), ora["o_sel"], "bf16", "o_sel")
-    rel = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"]) / np.maximum(
-        1.0, np.abs(ora["lse_sel"]))
-    assert rel.max() < 2e-3
+    for nm in ("out", "o_sel", "o_win", "o_cmp"):
+        assert_close(to_np(sv[nm]), ora[nm], "bf16", nm)
+    for nm in ("lse_sel", "lse_win"):
+        got = sv[nm].cpu().double().numpy()
+        rel = np.abs(got - ora[nm]) / np.maximum(1.0, np.abs(ora[nm]))
+        _print(nm, "max rel", rel.max())
+        assert rel.max() < 2e-3, (nm, rel.max())
 
 
-# ------------------------------------------------ full-size workloads, sampled rows
-def _sample_rows(T, n=24, seed=0):
-    rng = np.random.default_rng(seed)
-    fixed = [0, 63, 64, T // 2, T - 65, T - 64, T - 1]
-    return np.unique(np.concatenate([fixed, rng.integers(0, T, n)]))
+def test_large_logits_window_only_matches_oracle():
+    # the exact-maximum path with the selection skipped (window reference only)
+    wl = WORKLOADS["340m-gqa4"]
+    dev, f64 = device_inputs(wl, seq_len=1024, planted_sigma=1.0, q_scale=40.0)
+    _skip_flag_case(wl, dev, f64, nsa.SKIP_CMP_OUT | nsa.SKIP_SEL)
 
 
+# ------------------------------------------------ full-size workloads, every row
 @pytest.mark.parametrize("name", ["340m-gqa4", "1b3-gqa4", "mqa-ablation", "32k-fwd-bwd"])
-def test_full_size_workloads_on_sampled_rows(name):
+def test_full_size_workloads_every_row(name):
+    # Every row of the workload at its full size.  Indices: bit-exact where the
+    # oracle's gap is decisive, a valid top-m of the oracle's scores elsewhere.
+    # Outputs: every row against the oracle run on the GPU's own index table
+    # (the near-tie reading), so rows whose index sets differ are compared too.
     wl = WORKLOADS[name]
     _print("case full-size", name)
     dev, f64 = device_inputs(wl)
-    res = gpu_forward(wl, dev, want_indices=True)
+    res = gpu_forward(wl, dev, want_indices=True, want_lse=True, want_o_sel=True)
     torch.cuda.synchronize()
-    rows = _sample_rows(wl.seq_len)
-    ora = oracle_forward(wl, f64, rows=rows, want_scores=True)
-    agree = check_indices(res["indices"].cpu().numpy(), ora, wl.top_k, rows=rows,
-                          scores=ora["scores"])
-    m = rows_mask_from_groups(agree, wl.n_q_heads)
-    got = to_np(res["out"])[:, rows]
-    _print("agree", agree.mean(), "decisive", (ora["gap"][:, :, rows] > 1e-3).mean())
-    assert_close(got[m], ora["out"][:, rows][m], wl.dtype, "out")
+    gi = res["indices"].cpu().numpy()
+    ora = oracle_forward(wl, f64, want_scores=True)
+    agree = check_indices(gi, ora, wl.top_k, scores=ora["scores"])
+    decisive = ora["gap"] > 1e-3
+    _print(f"{name}: index sets equal on {agree.mean():.4f} of rows; decisive rows "
+           f"{decisive.mean():.4f}, all of them equal; rows compared 1.0000")
+    del ora
+    ora = oracle_forward(wl, f64, indices=gi)
+    assert_close(to_np(res["out"]), ora["out"], wl.dtype, "out")
+    assert_close(to_np(res["o_sel"]), ora["o_sel"], wl.dtype, "o_sel")
+    err = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"])
+    assert err.max() < LSE_TOL[wl.dtype], err.max()
     del dev
     torch.cuda.empty_cache()

@@ -119,6 +119,39 @@ def test_cmp_matches_sdpa_over_library_avgpool():
     assert np.all(r["o_cmp"][:, ~rows] == 0.0)
 
 
+def test_cmp_lse_matches_logsumexp_over_library_avgpool():
+    # The compressed branch's log-sum-exp: torch logsumexp of the scaled logits
+    # over avg_pool1d block means with the block-causal mask (block j visible
+    # iff 64(j+1)-1 <= t); -inf before the first block completes (t < 63).
+    B, T, Hq, Hkv, D = 2, 384, 4, 2, 16
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=31)
+    r = oracle.forward(q, k, v, g, top_k=3, window=32)
+    kt = torch.from_numpy(k).permute(0, 2, 3, 1).reshape(B * Hkv, D, T)
+    kc = F.avg_pool1d(kt, 64, 64).reshape(B, Hkv, D, -1).permute(0, 3, 1, 2).numpy()
+    nc = T // 64
+    vis = (np.arange(nc)[None, :] * 64 + 63) <= np.arange(T)[:, None]  # [T, nc]
+    want = sdpa_lse(q, kc, vis, 1.0 / np.sqrt(D))
+    rows = np.arange(T) >= 63
+    np.testing.assert_allclose(r["lse_cmp"][:, :, rows], want[:, :, rows], rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(r["lse_cmp"][:, :, ~rows]))
+
+
+def test_cmp_lse_constant_keys_closed_form():
+    # Every key of a KV head equal to c: each visible block mean is c, so the
+    # log-sum-exp is tau q.c + log n_c(t) exactly (up to rounding).
+    B, T, Hq, Hkv, D = 1, 320, 4, 2, 8
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=32)
+    c = np.random.default_rng(33).standard_normal((Hkv, D))
+    k[:] = c[None, None]
+    r = oracle.forward(q, k, v, g, top_k=3, window=16)
+    G, tau = Hq // Hkv, 1.0 / np.sqrt(D)
+    for t in [63, 64, 127, 128, 250, 319]:
+        nc = (t + 1) // 64
+        for h in range(Hq):
+            want = tau * q[0, t, h] @ c[h // G] + np.log(nc)
+            assert abs(r["lse_cmp"][0, h, t] - want) < 1e-12
+
+
 # ------------------------------------------------------------------ importance + top-k
 def test_scores_are_group_summed_softmax_probabilities():
     # The block importance is the compressed-branch attention probability summed
@@ -287,6 +320,23 @@ def test_window_matches_banded_sdpa():
     s, t = np.meshgrid(np.arange(T), np.arange(T))
     band = (s <= t) & (s > t - W)
     np.testing.assert_allclose(r["o_win"], sdpa(q, k, v, band, 1 / np.sqrt(D)), rtol=0, atol=1e-12)
+
+
+def test_window_lse_matches_banded_logsumexp():
+    # lse_win against torch logsumexp over the band t-W < s <= t, and the two
+    # closed forms: W >= T gives the causal log-sum-exp, W = 1 gives tau q_t.k_t.
+    B, T, Hq, Hkv, D, W = 1, 400, 4, 2, 8, 37
+    q, k, v, g = rand_inputs(B, T, Hq, Hkv, D, seed=34)
+    tau = 1.0 / np.sqrt(D)
+    s, t = np.meshgrid(np.arange(T), np.arange(T))
+    band = (s <= t) & (s > t - W)
+    r = oracle.forward(q, k, v, g, top_k=2, window=W)
+    np.testing.assert_allclose(r["lse_win"], sdpa_lse(q, k, band, tau), rtol=0, atol=1e-12)
+    r = oracle.forward(q, k, v, g, top_k=2, window=T + 5)
+    np.testing.assert_allclose(r["lse_win"], sdpa_lse(q, k, causal_mask(T), tau), rtol=0, atol=1e-12)
+    r = oracle.forward(q, k, v, g, top_k=2, window=1)
+    own = tau * np.einsum("bthd,bthd->bht", q, np.repeat(k, Hq // Hkv, axis=2))
+    np.testing.assert_allclose(r["lse_win"], own, rtol=0, atol=1e-12)
 
 
 # ------------------------------------------------------------------------- combine
