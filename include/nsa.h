@@ -156,6 +156,28 @@ nsa_status_t nsa_forward(const void* q, const void* k, const void* v, const void
                          const nsa_params_t* p, void* out, int32_t* indices, float* lse_sel,
                          void* o_sel, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the fixed per-GPU scratch array that nsa_forward_noalloc uses as
+ * its workspace (32 MiB; a forward whose nsa_workspace_size(p, 0) exceeds it,
+ * e.g. batch 1 at seq 8192 with 16 heads of 64 needs about 26 MiB, is
+ * rejected). */
+#define NSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* nsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, checks, kernels and results, but no workspace argument --
+ * it uses a fixed static device array of NSA_NOALLOC_SCRATCH_BYTES per GPU,
+ * which the library holds from load until the process ends.  Nothing is
+ * allocated or freed.  Returns NSA_ERR_WORKSPACE (before any launch) when
+ * nsa_workspace_size(p, 0) > NSA_NOALLOC_SCRATCH_BYTES, NSA_ERR_LAUNCH if the
+ * array's device address cannot be looked up.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and must be serialised by the
+ * caller.  The array keeps the previous call's contents; the forward rewrites
+ * everything it reads. */
+nsa_status_t nsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gates,
+                                 const nsa_params_t* p, void* out, int32_t* indices,
+                                 float* lse_sel, void* o_sel, void* stream);
+
 /* nsa_forward, plus stage timing for measurement: `events` points to four
  * caller-created hipEvent_t handles (passed as void*; any may be NULL), which
  * are recorded on `stream` before the compression kernel, after it, after the

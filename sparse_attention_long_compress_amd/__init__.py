@@ -22,7 +22,9 @@ EXPORTED = (
     "nsa_workspace_size",
     "nsa_pool", "nsa_compress_select", "nsa_forward", "nsa_forward_profile", "nsa_select_bwd",
     "nsa_forward_train", "nsa_backward", "nsa_select_bwd_single", "nsa_decode",
+    "nsa_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class NsaError(RuntimeError):
@@ -78,6 +80,8 @@ def lib():
         L.nsa_forward_profile.argtypes = [vp, vp, vp, vp, P, vp, i32p, f32p, vp, vp,
                                           ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_void_p)]
         L.nsa_forward_profile.restype = ctypes.c_int
+        L.nsa_forward_noalloc.argtypes = [vp, vp, vp, vp, P, vp, i32p, f32p, vp, vp]
+        L.nsa_forward_noalloc.restype = ctypes.c_int
         L.nsa_select_bwd.argtypes = [vp, vp, vp, vp, i32p, f32p, vp, vp, P, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
         L.nsa_select_bwd.restype = ctypes.c_int
@@ -231,6 +235,22 @@ def forward(q, k, v, gates, *, top_k, window, scale=None, flags=0, indices=None,
     if o_sel is not None:
         res["o_sel"] = o_sel
     return res
+
+
+def forward_noalloc(q, k, v, gates, *, top_k, window, scale=None, flags=0, indices=None,
+                    out, indices_out=None, lse_sel=None, o_sel=None, stream=None):
+    """NSA forward without a workspace (nsa_forward_noalloc: the library's fixed
+    per-GPU scratch array).  Every output tensor is the caller's: ``out`` and,
+    as wanted, ``indices_out`` [B,Hkv,T,top_k] int32, ``lse_sel`` [B,Hq,T]
+    fp32, ``o_sel``; ``indices`` given sets INDICES_IN.  Allocates nothing."""
+    if indices is not None:
+        flags |= INDICES_IN
+        indices_out = indices
+    p = params_for(q, k, top_k=top_k, window=window, scale=scale, flags=flags)
+    _check(lib().nsa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(gates), ctypes.byref(p),
+                                     _ptr(out), _ptr(indices_out), _ptr(lse_sel), _ptr(o_sel),
+                                     _stream(stream)), "nsa_forward_noalloc")
+    return out
 
 
 def select_bwd(q, k, v, gates, indices, lse_sel, o_sel, dout, *, top_k, scale=None,

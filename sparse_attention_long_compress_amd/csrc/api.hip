@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/nsa.h"
 #include "nsa_launch.h"
 
@@ -292,6 +294,51 @@ nsa_status_t nsa_forward(const void* q, const void* k, const void* v, const void
                          void* o_sel, void* workspace, size_t ws_bytes, void* stream) {
   return nsa_forward_profile(q, k, v, gates, p, out, indices, lse_sel, o_sel, workspace, ws_bytes,
                              stream, nullptr);
+}
+
+}  // extern "C"
+
+// Workspace of nsa_forward_noalloc: one fixed device array per GPU, held from
+// the library's load until the process ends.  In host code `scratch` only
+// names the symbol; its device address (per device) comes from
+// hipGetSymbolAddress and is the only form ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[NSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (nullptr: not yet)
+
+// Device address of this device's scratch array (looked up once per device,
+// with that device current).  nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+nsa_status_t nsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gates,
+                                 const nsa_params_t* p, void* out, int32_t* indices,
+                                 float* lse_sel, void* o_sel, void* stream) {
+  nsa_status_t st = check(p);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !gates || !out) return NSA_ERR_NULL;
+  if ((p->flags & NSA_INDICES_IN) && !indices) return NSA_ERR_NULL;
+  const Shape s = make_shape(p);
+  if (fwd_layout(s, esize(p)).total > (size_t)NSA_NOALLOC_SCRATCH_BYTES) return NSA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return NSA_ERR_LAUNCH;
+  return forward_impl(q, k, v, gates, p, out, indices, lse_sel, o_sel, nullptr, nullptr, nullptr,
+                      nullptr, ws, (size_t)NSA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 nsa_status_t nsa_select_bwd(const void* q, const void* k, const void* v, const void* gates,

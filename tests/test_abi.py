@@ -143,3 +143,19 @@ def test_other_entry_points_argument_errors():
     assert L.nsa_select_bwd(*args, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, wsb - 1, None) == EWS
     args[4] = None
     assert L.nsa_select_bwd(*args, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, wsb, None) == ENULL
+
+
+def test_noalloc_argument_errors_launch_nothing():
+    # checked before the scratch array's device address is looked up: no GPU needed
+    L = nsa.lib()
+    f = ctypes.c_void_p(FAKE)
+    small = params(T=8192, Hq=16, Hkv=4, top_k=16, window=512)
+    assert L.nsa_workspace_size(ctypes.byref(small), 0) <= nsa.NOALLOC_SCRATCH_BYTES
+    assert L.nsa_forward_noalloc(None, f, f, f, ctypes.byref(small), f, None, None, None, None) == ENULL
+    idx_in = params(T=8192, Hq=16, Hkv=4, top_k=16, window=512, flags=nsa.INDICES_IN)
+    assert L.nsa_forward_noalloc(f, f, f, f, ctypes.byref(idx_in), f, None, None, None, None) == ENULL
+    big = params(B=4, T=8192, Hq=16, Hkv=4, D=128, top_k=16, window=512)
+    assert L.nsa_workspace_size(ctypes.byref(big), 0) > nsa.NOALLOC_SCRATCH_BYTES
+    assert L.nsa_forward_noalloc(f, f, f, f, ctypes.byref(big), f, None, None, None, None) == EWS
+    assert L.nsa_forward_noalloc(f, f, f, f, ctypes.byref(params(D=96)), f, None, None, None,
+                                 None) == EUNSUP
