@@ -7,12 +7,19 @@ oracle's selection exactly.
 Tolerances: the pages give none for gradients.  Reading used here: the
 forward's bounds scaled by the gradient's root-mean-square magnitude --
 max-abs <= 2e-2 * max(1, rms_ref) and mean-abs <= 2e-3 * max(1, rms_ref) for
-bf16, 1e-4 * max(1, rms_ref) for fp32 -- with one addition for bf16: every
-product in a gradient sum has both operands rounded to bf16 once (P, dS and
-g_sel dO; unit roundoff 2^-8 each), so an element carries a relative error of
-up to 2^-7 of its own magnitude on top of that (its size is set by its own
-terms, e.g. the first keys, which few queries share, get gradients ~50x the
-rms).  Each case prints its measured errors."""
+bf16, 1e-4 * max(1, rms_ref) for fp32 -- with one addition for bf16: each
+product in a gradient sum has operands that carry up to four bf16 unit
+roundoffs (2^-8 each) of relative error -- P rounded for the MFMA and
+normalised by the saved log-sum-exp (itself a sum of bf16-rounded
+probabilities), dS = P (dP - Delta) rounded, g_sel dO rounded -- so an element
+may also be off by 2^-6 of its own magnitude (elements are as large as their
+own terms make them: the first keys, which few queries share, get gradients
+~50x the rms).  dk and dv of one key sum the terms of all G query heads of its
+group: with rounding errors of independent sign, their spread grows as the
+square root of the number of terms, so for G > 4 (more heads per key than the
+GQA-4 workloads the bound was set on) the max-abs allowance is scaled by
+sqrt(G / 4).  Each case prints its measured errors."""
+
 import numpy as np
 import pytest
 import torch
@@ -25,16 +32,17 @@ from tests.nsa_cases import device_inputs, oracle_forward, to_np
 pytestmark = pytest.mark.gpu
 
 
-REL_BF16 = 2.0 ** -7
+REL_BF16 = 2.0 ** -6
 
 
-def grad_close(got, ref, dtype, what):
+def grad_close(got, ref, dtype, what, heads_per_key=1):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     rms = max(1.0, float(np.sqrt((ref ** 2).mean())))
     err = np.abs(got - ref)
     mx, mean = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
+    mx *= np.sqrt(max(1.0, heads_per_key / 4.0))
     rel = REL_BF16 if dtype == "bf16" else 0.0
     excess = float((err - rel * np.abs(ref)).max())
     print(f"{what}: max|ref| {np.abs(ref).max():.3g} rms_ref {np.sqrt((ref ** 2).mean()):.3g} "
@@ -81,8 +89,9 @@ def test_select_bwd_matches_oracle(name, T, over):
     wl = WORKLOADS[name].with_(**over)
     print("case", name, T, over, flush=True)
     got, ref, *_ = run_both(wl, T)
+    G = wl.n_q_heads // wl.n_kv_heads
     for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
-        grad_close(to_np(g_), r_, wl.dtype, nm)
+        grad_close(to_np(g_), r_, wl.dtype, nm, heads_per_key=1 if nm == "dq" else G)
 
 
 def test_select_bwd_full_size_340m():
@@ -149,5 +158,6 @@ def test_single_pass_atomic_backward_matches_oracle(name, T, over):
     got = nsa.select_bwd_single(dev["q"], dev["k"], dev["v"], dev["gates"], idx, fwd["lse_sel"],
                                 fwd["o_sel"], dev["dout"], top_k=wl.top_k, scale=wl.scale)
     torch.cuda.synchronize()
+    G = wl.n_q_heads // wl.n_kv_heads
     for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
-        grad_close(to_np(g_), r_, wl.dtype, nm)
+        grad_close(to_np(g_), r_, wl.dtype, nm, heads_per_key=1 if nm == "dq" else G)
