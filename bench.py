@@ -11,8 +11,9 @@ Prints ONE JSON line (rank 0, N = 1):
   value      = forward tokens/s = batch * seq_len / (seconds per forward step)
   roofline   = the selection/window/combine kernel (the dominant one): useful
                attention FLOPs per launch / its average duration, measured with
-               HIP events recorded around it on its own stream in every timed
-               step, against the bf16 dense MFMA peak
+               HIP events recorded around it on its own stream in K steps run
+               right after the timed ones (the events would perturb the timed
+               steps), against the bf16 dense MFMA peak
   cpu_baseline = the fp64 oracle timed on the host (every core this process
                may use; nproc and CPU model stated) on a bounded sample of the
                same workload: whole forward passes, about ten seconds of them
@@ -262,15 +263,15 @@ def decode_bench(nsa, torch, np, wl, steps, warmup, batch=64):
         nsa.decode(q, k, v, kc, vc, lens, gates, top_k=wl.top_k, window=wl.window,
                    scale=wl.scale, out=out)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for e0, e1 in evs:
-        e0.record()
+    # one event pair around all the steps (events between steps perturb them)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         nsa.decode(q, k, v, kc, vc, lens, gates, top_k=wl.top_k, window=wl.window,
                    scale=wl.scale, out=out)
-        e1.record()
+    e1.record()
     torch.cuda.synchronize()
-    dt = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e-3
+    dt = e0.elapsed_time(e1) * 1e-3 / steps
     gbs = nbytes / dt / 1e9
     return {"kernel": "decode_mfma_kernel" if wl.dtype == "bf16" else "decode_kernel",
             "batch": batch, "cache_len": Lmax,
@@ -296,8 +297,11 @@ def prepare(wl, with_dout):
 
 def time_forward(nsa, torch, np, wl, dev, steps, warmup, branches="all"):
     """Forward steps of the workload timed with the host clock (bracketed by
-    synchronisations) and per kernel with HIP events recorded by the library
-    around each of its three kernels on the launch stream."""
+    synchronisations): the throughput.  Then the same number of steps again
+    with HIP events recorded by the library around each of its three kernels
+    on the launch stream: the per-kernel durations (recording those events
+    costs about 35 us of a 190 us step, so they are kept out of the
+    throughput region)."""
     bflags = {"all": 0, "no-cmp": nsa.SKIP_CMP_OUT,
               "window": nsa.SKIP_CMP_OUT | nsa.SKIP_SEL}[branches]
     p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale,
@@ -313,6 +317,11 @@ def time_forward(nsa, torch, np, wl, dev, steps, warmup, branches="all"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
     # events (created by torch on the current stream's device; raw handles go to the library)
     evs = []
     for _ in range(steps):
@@ -321,11 +330,9 @@ def time_forward(nsa, torch, np, wl, dev, steps, warmup, branches="all"):
             e.record()  # materialise the underlying hipEvent_t
         evs.append(row)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(events=[e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
     k1 = np.mean([r[0].elapsed_time(r[1]) for r in evs]) * 1e-3
     k2 = np.mean([r[1].elapsed_time(r[2]) for r in evs]) * 1e-3
     k3 = np.mean([r[2].elapsed_time(r[3]) for r in evs]) * 1e-3
@@ -367,14 +374,14 @@ def time_select_bwd(nsa, torch, np, wl, dev, ws, steps, warmup):
     for _ in range(warmup):
         bstep()
     torch.cuda.synchronize()
-    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for e0, e1 in bev:
-        e0.record()
+    # one event pair around all the calls (events between calls perturb them)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         bstep()
-        e1.record()
+    e1.record()
     torch.cuda.synchronize()
-    bwd = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bev])) * 1e-3
+    bwd = e0.elapsed_time(e1) * 1e-3 / steps
     fb = useful_bwd_flops(wl)
     return bwd, {"us": round(bwd * 1e6, 2), "useful_tflops": round(fb / bwd / 1e12, 2),
                  "pct_bf16_peak": round(100 * fb / bwd / 1e12 / PEAK_BF16_TFLOPS, 2)}
@@ -532,24 +539,30 @@ def main():
         fgrads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]),
                   torch.empty_like(dev["gates"]))
 
-        def tstep(e):
-            e[0].record()
+        def fstep():
             nsa.forward_train(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
                               window=wl.window, scale=wl.scale, workspace=ws, out=saved["out"])
-            e[1].record()
+
+        def bwstep():
             nsa.backward(dev["q"], dev["k"], dev["v"], dev["gates"], saved, dev["dout"],
                          top_k=wl.top_k, window=wl.window, scale=wl.scale, workspace=wsf,
                          out=fgrads)
-            e[2].record()
 
-        tev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-               for _ in range(args.warmup + args.steps)]
-        for i in range(args.warmup + args.steps):
-            tstep(tev[i])
+        def loop_time(fn):
+            # one event pair around all the calls (events between calls perturb them)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / args.steps
+
+        for _ in range(args.warmup):
+            fstep()
+            bwstep()
         torch.cuda.synchronize()
-        tev = tev[args.warmup:]
-        train = (float(np.mean([e[0].elapsed_time(e[1]) for e in tev])) * 1e-3,
-                 float(np.mean([e[1].elapsed_time(e[2]) for e in tev])) * 1e-3)
+        train = (loop_time(fstep), loop_time(bwstep))
         del wsf, saved, fgrads
 
     tokens = wl.batch * wl.seq_len
