@@ -598,6 +598,8 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         }
       } else {
         // causal diagonal, window edge, or rows with two exact references
+        // (one exponential per element serves both branches unless the exact
+        // references differ)
         const float ms = sl[cg] ? mr_s[cg] : INF, mw = wl[cg] ? mr_w[cg] : INF;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -608,8 +610,15 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
             const float x = st[cg][u][rr] * c1;
             const int key = j * kBlock + key_of(u, a, rr);
             const bool caus = key <= tp;
-            pv[e] = caus ? fast_exp2(x - ms) : 0.f;
-            qw[e] = (caus && key > tp - W) ? fast_exp2(x - mw) : 0.f;
+            const bool inw = caus && key > tp - W;
+            if (!exact) {
+              const float ex = fast_exp2(x - mr_s[cg]);  // mr_s == mr_w
+              pv[e] = caus && sl[cg] ? ex : 0.f;
+              qw[e] = inw && wl[cg] ? ex : 0.f;
+            } else {
+              pv[e] = caus ? fast_exp2(x - ms) : 0.f;
+              qw[e] = inw ? fast_exp2(x - mw) : 0.f;
+            }
           }
           ps[cg][hf] = Frag<T>::from_f32(pv);
           pw[cg][hf] = Frag<T>::from_f32(qw);

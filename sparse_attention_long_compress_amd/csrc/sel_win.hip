@@ -185,20 +185,24 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
     own[cg] = (t0 + p0) / kBlock;  // NSG divides 64: one own block per column group
     valid[cg] = p < nvalid;
     ptr[cg] = 0;
+    // every load of the row is issued before the first is used; rows past
+    // the ragged end read the last row and are zeroed afterwards
+    const int tr = min(tpos[cg], s.T - 1);
+    FragT kv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[cg][ks] = Frag<T>::load(q + ((size_t)b * s.T + tr) * q_row + (size_t)h * D + ks * 32 + 8 * a);
+      kv[ks] = Frag<T>::load(k_b + (size_t)tr * k_row + ks * 32 + 8 * a);
+    }
     float qq = 0.f, d = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (valid[cg]) {
-        qf[cg][ks] = Frag<T>::load(q + ((size_t)b * s.T + tpos[cg]) * q_row + (size_t)h * D + ks * 32 + 8 * a);
-        const FragT kv = Frag<T>::load(k_b + (size_t)tpos[cg] * k_row + ks * 32 + 8 * a);
+      if (!valid[cg]) qf[cg][ks] = Frag<T>::zero();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)qf[cg][ks][e];
-          qq += x * x;
-          d += x * (float)kv[e];
-        }
-      } else {
-        qf[cg][ks] = Frag<T>::zero();
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qf[cg][ks][e];
+        qq += x * x;
+        d += x * (float)kv[ks][e];
       }
     }
     qq = xsum4(qq);
@@ -489,17 +493,34 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
   }
 
   // ------------------------------------------------------------ combine
+  // Gates and the compressed output of every row are loaded before the first
+  // store so that the loads overlap; rows past the ragged end read the last
+  // row and store nothing.
   const T* gates = (const T*)args.gates;
   T* out = (T*)args.out;
+  float g3[NCG][3];
+  f32x4 oc[NCG][MT];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int tr = min(tpos[cg], s.T - 1);
+    const T* grow = gates + (((size_t)b * s.T + tr) * s.Hq + h) * 3;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) g3[cg][e] = to_f32(grow[e]);
+    const size_t rb = ((size_t)b * s.T + tr) * q_row + (size_t)h * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oc[cg][mt] = load4((const T*)args.o_cmp + rb + mt * 16 + 4 * a);
+  }
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const float ls = xsum4(l_s[cg]), lw = xsum4(l_w[cg]);
     if (!valid[cg]) continue;
     const int t = tpos[cg];
-    const T* grow = gates + (((size_t)b * s.T + t) * s.Hq + h) * 3;
-    const float gc = cmp_on ? to_f32(grow[0]) : 0.f;
-    const float gs = sel_on ? to_f32(grow[1]) : 0.f;
-    const float gw = win_on ? to_f32(grow[2]) : 0.f;
+    // the compressed branch has no block for the first 63 positions; its
+    // buffer is then left unwritten, so it is selected, not scaled by zero
+    const bool use_c = cmp_on && t >= kBlock - 1;
+    const float gc = g3[cg][0];
+    const float gs = sel_on ? g3[cg][1] : 0.f;
+    const float gw = win_on ? g3[cg][2] : 0.f;
     const float iw = win_on ? gw / lw : 0.f;
     const float ilw = win_on ? 1.f / lw : 0.f;
     const float il = need_sel ? 1.f / ls : 0.f;
@@ -514,7 +535,7 @@ __global__ __launch_bounds__((K3Cfg<T, D, G>::NT), (K3Cfg<T, D, G>::WGPC)) void 
         if (sel_on) res += os * gs;
         if (args.o_sel) store4((T*)args.o_sel + obase + d0, os);
       }
-      if (cmp_on && t >= kBlock - 1) res += load4((const T*)args.o_cmp + obase + d0) * gc;
+      if (use_c) res += oc[cg][mt] * gc;
       store4(out + obase + d0, res);
     }
     if (args.lse && a == 0) args.lse[((size_t)b * s.Hq + h) * s.T + t] = (mr_s[cg] + __log2f(ls)) * kLn2;
