@@ -210,24 +210,30 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
     stage(jb, true);
     __syncthreads();
     for (int h = 0; h < 2 && jb + h * 32 < nvis; ++h) {
+      // blocks below the tile's own block are visible to every row of it (and
+      // complete): only a half that reaches block c needs the per-element mask
+      const bool full = jb + h * 32 + 31 < c;
 #pragma unroll
       for (int cg = 0; cg < CGW; ++cg) {
-        float x[8], pv[8];
+        float x[8], pv[8];  // raw scores (the scale c1 > 0 is applied in the exponent)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const f32x4 st = scores(h, u, qf[cg]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int jj = jb + h * 32 + 8 * a + 4 * u + r;
-            const bool vis = (jj * kBlock + kBlock - 1 <= tpos[cg]) && jj < s.nc;
-            const float xv = st[r] * c1;
-            x[4 * u + r] = vis ? xv : -INFINITY;
+            if (full) {
+              x[4 * u + r] = st[r];
+            } else {
+              const int jj = jb + h * 32 + 8 * a + 4 * u + r;
+              const bool vis = (jj * kBlock + kBlock - 1 <= tpos[cg]) && jj < s.nc;
+              x[4 * u + r] = vis ? st[r] : -INFINITY;
+            }
           }
         }
         float mx = x[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-        mx = xmax4(mx);
+        mx = xmax4(mx) * c1;
         const float mn = fmaxf(m[cg], mx);
         float alpha = 1.f, psum = 0.f;
         if (mn == -INFINITY) {
@@ -236,7 +242,7 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
         } else {
           alpha = fast_exp2(m[cg] - mn);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { pv[e] = fast_exp2(x[e] - mn); psum += pv[e]; }
+          for (int e = 0; e < 8; ++e) { pv[e] = fast_exp2(fmaf(x[e], c1, -mn)); psum += pv[e]; }
         }
         lsum[cg] = lsum[cg] * alpha + xsum4(psum);
         m[cg] = mn;
@@ -269,9 +275,15 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
   const float qscale = 2097152.f / (float)G;
 
   if (need_scores) {
-    for (int jb = 1; jb <= c - 1; jb += 64) {
-      __syncthreads();
-      stage(jb, false);
+    // candidates 1 .. c - 1 in the 64-block chunks of pass 1, last chunk first:
+    // when it is pass 1's last chunk its keys are still in LDS
+    const int jb_last1 = (nvis - 1) / 64 * 64;  // pass 1's last chunk
+    const int jb_top = (c - 1) / 64 * 64;
+    for (int jb = jb_top; jb >= 0; jb -= 64) {
+      if (jb != jb_last1) {
+        __syncthreads();
+        stage(jb, false);
+      }
       __syncthreads();
       for (int h = 0; h < 2 && jb + h * 32 <= c - 1; ++h) {
 #pragma unroll
@@ -284,7 +296,7 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
               const int jj = jb + h * 32 + 8 * a + 4 * u + r;
               float pr = fast_exp2(st[r] * c1 - lse2[cg]);
               pr = group_sum<G>(pr);
-              if ((col % G) == 0 && jj <= c - 1) S_l[ppos[cg]][jj - jb] = pr;
+              if ((col % G) == 0 && jj >= 1 && jj <= c - 1) S_l[ppos[cg]][jj - jb] = pr;
             }
           }
         }
@@ -294,7 +306,7 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
       // position: all read at once, sorted by a network, merged into the list
       // (a missing candidate is key 0)
       if (l < P) {
-        const int j0 = jb + CPW * w, j1 = min(jb + CPW * w + CPW, c);
+        const int j0 = max(jb + CPW * w, 1), j1 = min(jb + CPW * w + CPW, c);
         uint32_t cand[LMAX];
 #pragma unroll
         for (int k = 0; k < LMAX; ++k)
@@ -324,32 +336,28 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
     }
   }
 
+  // The row's selection in increasing block order: block 0, the picks (all in
+  // 1 .. c - 1) sorted, the own block c.  Without scores every block 0 .. c
+  // is selected.
   if (w == 0 && l < P) {
     const int t = t0 + l;
-    constexpr int KMAX = LMAX + 2;
-    int sel[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) sel[i] = 0x7fffffff;
-    int n = 0;
-    auto ins = [&](int x) {
-#pragma unroll
-      for (int i = KMAX - 1; i >= 1; --i) sel[i] = max(min(sel[i], x), min(max(sel[i], x), sel[i - 1]));
-      sel[0] = min(sel[0], x);
-      ++n;
-    };
-    ins(0);
-    if (c > 0) ins(c);
+    int32_t* dst = indices + (((size_t)b * s.Hkv + g) * s.T + t) * s.topk;
     if (!need_scores) {
-      for (int j = 1; j <= c - 1; ++j) ins(j);
+      for (int i = 0; i < s.topk; ++i) dst[i] = i <= c ? i : -1;
     } else {
+      // block indices of the picks (list is sorted by score), unused slots
+      // last, sorted ascending
+      uint32_t pk[LMAX];
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) pk[i] = i < m_free ? ~(kIdxMask - (list[i] & kIdxMask)) : 0u;
+      sort_desc(pk);  // descending in ~j: ascending in j
+      dst[0] = 0;
 #pragma unroll
       for (int i = 0; i < LMAX; ++i)
-        if (i < m_free) ins((int)(kIdxMask - (list[i] & kIdxMask)));
+        if (i < m_free) dst[1 + i] = (int32_t)~pk[i];
+      dst[1 + m_free] = c;
+      for (int i = m_free + 2; i < s.topk; ++i) dst[i] = -1;
     }
-    int32_t* dst = indices + (((size_t)b * s.Hkv + g) * s.T + t) * s.topk;
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i)
-      if (i < s.topk) dst[i] = i < n ? sel[i] : -1;
   }
 }
 
