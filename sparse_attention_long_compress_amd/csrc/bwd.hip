@@ -205,24 +205,48 @@ __global__ __launch_bounds__(256) void bwd_pool_image_kernel(Shape s, const T* _
 
 // ============================================================ B1: reverse map
 // grid (nblk tiles c, Hkv, B), 64 threads (lane = position of the tile).
-// revmap[b][g][j][c] for j <= c, built with 64-bit LDS ORs.
+// revmap[b][g][j][c] for j <= c: each lane's chosen blocks as a bit row in
+// registers, then one wave ballot per block (no LDS, no atomics).
+template <int MW>  // bit-row words per lane: blocks 0 .. 32 MW - 1
 __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* __restrict__ idx,
                                                         uint64_t* __restrict__ revmap) {
-  extern __shared__ unsigned long long msk[];  // [c + 1]
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nblk = s.T / kBlock;
   const int l = threadIdx.x;
-  for (int i = l; i <= c; i += 64) msk[i] = 0ull;
-  __syncthreads();
   const int t = c * kBlock + l;
   const int32_t* row = idx + (((size_t)b * s.Hkv + g) * s.T + t) * s.topk;
+  // the blocks this lane's position chose, as a bit row in registers (word w:
+  // blocks 32 w .. 32 w + 31); indices outside 0 .. c are ignored
+  unsigned bits[MW];
+#pragma unroll
+  for (int w = 0; w < MW; ++w) bits[w] = 0u;
   for (int e = 0; e < s.topk; ++e) {
     const int j = row[e];
-    if (j >= 0 && j <= c) atomicOr(&msk[j], 1ull << l);
+    if (j < 0 || j > c) continue;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) bits[w] |= (j >> 5) == w ? 1u << (j & 31) : 0u;
   }
-  __syncthreads();
+  // Block j's mask of positions is one wave ballot over bit j of the rows; lane
+  // j % 64 keeps it, and the lanes store their blocks' masks together at the end.
+  constexpr int MQ = (MW + 1) / 2;  // masks per lane
+  uint64_t keep[MQ];
+#pragma unroll
+  for (int q = 0; q < MQ; ++q) keep[q] = 0ull;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) {
+    if (32 * w > c) break;
+    const int kn = min(32, c + 1 - 32 * w);
+    for (int k = 0; k < kn; ++k) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64((bits[w] >> k) & 1u);
+      if (l == ((32 * w + k) & 63)) keep[w / 2] = m;
+    }
+  }
   uint64_t* dst = revmap + (((size_t)b * s.Hkv + g) * nblk) * nblk + c;
-  for (int j = l; j <= c; j += 64) dst[(size_t)j * nblk] = msk[j];
+#pragma unroll
+  for (int q = 0; q < MQ; ++q) {
+    const int j = 64 * q + l;
+    if (j <= c) dst[(size_t)j * nblk] = keep[q];
+  }
 }
 
 // ============================================================ launchers
@@ -273,7 +297,12 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
                              hipStream_t st) {
   const int nblk = s.T / kBlock;
   dim3 grid(nblk, s.Hkv, s.B);
-  hipLaunchKernelGGL(bwd_revmap_kernel, grid, dim3(64), (size_t)nblk * 8, st, s, indices, revmap);
+  if (nblk <= 128)
+    hipLaunchKernelGGL(bwd_revmap_kernel<4>, grid, dim3(64), 0, st, s, indices, revmap);
+  else if (nblk <= 256)
+    hipLaunchKernelGGL(bwd_revmap_kernel<8>, grid, dim3(64), 0, st, s, indices, revmap);
+  else  // sequences up to 65536: 1024 blocks
+    hipLaunchKernelGGL(bwd_revmap_kernel<32>, grid, dim3(64), 0, st, s, indices, revmap);
   return hipGetLastError();
 }
 

@@ -63,6 +63,11 @@
 #ifndef NSA_K3_FCH128
 #define NSA_K3_FCH128 2
 #endif
+// (one query head per KV group: the column group is 16 positions, and wider
+// read batches measured faster at sequence 8192)
+#ifndef NSA_K3_FCH128_G1
+#define NSA_K3_FCH128_G1 4
+#endif
 // packed selection items for the shapes sel_compact.hip covers (0: general kernel)
 #ifndef NSA_K3_COMPACT
 #define NSA_K3_COMPACT 1
@@ -92,7 +97,7 @@ struct K3Cfg {
   static constexpr int NV = Img::NV;              // 16-byte pieces per lane fragment
   static constexpr int EPV = Img::EPV;            // elements per piece and lane
   static constexpr int NFRAG = Img::NFRAG;        // fragments per operand and block (4 KS = 2 MT)
-  static constexpr int FCH_ = WIDE ? NSA_K3_FCH128 : NSA_K3_FCH64;
+  static constexpr int FCH_ = WIDE ? (G == 1 ? NSA_K3_FCH128_G1 : NSA_K3_FCH128) : NSA_K3_FCH64;
   static constexpr int FCH = (NFRAG < FCH_ ? NFRAG : FCH_) / NV;  // fragments per LDS read batch
   static constexpr int FRAG_BYTES = NV * 1024;
   static constexpr int STAGE = Img::BYTES;        // one block's image: K fragments, then V^T
