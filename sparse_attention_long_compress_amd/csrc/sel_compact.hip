@@ -416,6 +416,9 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     return e;
   };
 
+  FragT ones;  // all-ones MFMA operand (row sums)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
   // stage B of the pending items: exponentials, P V over the block's V^T
   // (vst), row sums, then the rows' accumulator update
   auto finish_items = [&](const unsigned char* vst) __attribute__((always_inline)) {
@@ -443,10 +446,16 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sB[x][2 * hf + e / 4][e % 4] * c1 - mB[x]);
         dp[hf] = Frag<T>::from_f32(pv);
       }
-      const float dl = xsum4(frag_sum(dp[0]) + frag_sum(dp[1]));
+      // P V is accumulated onto the rows' current sums (the MFMA's C operand),
+      // and the row sum of P (the bf16 values P V uses) is an MFMA against an
+      // all-ones A operand: both on the matrix unit, not the VALU
+      f32x4 rs = zero4();
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) rs = mma(rs, ones, dp[hf]);
+      const float dl = rs[0];
       f32x4 o1[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o1[mt] = zero4();
+      for (int mt = 0; mt < MT; ++mt) o1[mt] = cur[mt];
 #pragma unroll
       for (int f0 = 0; f0 < NFRAG; f0 += KF) {
         if constexpr (KF != NFRAG) {
@@ -457,10 +466,10 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         for (int i2 = 0; i2 < KF; ++i2)
           o1[Img::v_mt(f0 + i2)] = mma(o1[Img::v_mt(f0 + i2)], vf[i2], dp[Img::v_h(f0 + i2)]);
       }
-      if (vB[x]) {
+      if (vB[x]) {  // (unused columns read rows 0 .. 3 and must not write them)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(rowp + 16 * mt + 4 * a) = cur[mt] + o1[mt];
+          *reinterpret_cast<f32x4*>(rowp + 16 * mt + 4 * a) = o1[mt];
         if (a == 0) rowp[kcD] += dl;
       }
     }
