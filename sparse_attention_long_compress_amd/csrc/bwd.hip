@@ -14,7 +14,8 @@
 //              (K, V, K^T fragments) for B2 and B3.
 // B1 revmap  : M[b][g][j][c] = 64-bit mask of the positions of tile c (64
 //              positions) that selected block j -- one wave per (tile, group),
-//              one lane per position, a ballot per block; no atomics.
+//              one lane per position, a bit-matrix transpose by lane
+//              exchanges; no atomics.
 // B2 dq      : query-stationary, the block walk of the forward's selection
 //              kernel (bwd_dq.hip).
 // B3 dk/dv   : key/value-stationary over the rows of M (bwd_dkdv.hip); blocks
@@ -205,9 +206,16 @@ __global__ __launch_bounds__(256) void bwd_pool_image_kernel(Shape s, const T* _
 
 // ============================================================ B1: reverse map
 // grid (nblk tiles c, Hkv, B), 64 threads (lane = position of the tile).
-// revmap[b][g][j][c] for j <= c: each lane's chosen blocks as a bit row in
-// registers, then one wave ballot per block (no LDS, no atomics).
-template <int MW>  // bit-row words per lane: blocks 0 .. 32 MW - 1
+// revmap[b][g][j][c] for j <= c, per 64-block chunk q: lane l builds its
+// position's row of a 64 x 64 bit matrix (bit i: block 64 q + i chosen), and a
+// transpose of that matrix by six butterfly stages of lane exchanges (shuffles,
+// no LDS table, no atomics) leaves in lane l the positions that chose block
+// 64 q + l.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)x, m);
+  const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
 __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* __restrict__ idx,
                                                         uint64_t* __restrict__ revmap) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -215,37 +223,40 @@ __global__ __launch_bounds__(64) void bwd_revmap_kernel(Shape s, const int32_t* 
   const int l = threadIdx.x;
   const int t = c * kBlock + l;
   const int32_t* row = idx + (((size_t)b * s.Hkv + g) * s.T + t) * s.topk;
-  // the blocks this lane's position chose, as a bit row in registers (word w:
-  // blocks 32 w .. 32 w + 31); indices outside 0 .. c are ignored
-  unsigned bits[MW];
+  // (the row's loads all go out before the first is used: top-k <= 32)
+  int jv[32];
 #pragma unroll
-  for (int w = 0; w < MW; ++w) bits[w] = 0u;
-  for (int e = 0; e < s.topk; ++e) {
-    const int j = row[e];
-    if (j < 0 || j > c) continue;
-#pragma unroll
-    for (int w = 0; w < MW; ++w) bits[w] |= (j >> 5) == w ? 1u << (j & 31) : 0u;
-  }
-  // Block j's mask of positions is one wave ballot over bit j of the rows; lane
-  // j % 64 keeps it, and the lanes store their blocks' masks together at the end.
-  constexpr int MQ = (MW + 1) / 2;  // masks per lane
-  uint64_t keep[MQ];
-#pragma unroll
-  for (int q = 0; q < MQ; ++q) keep[q] = 0ull;
-#pragma unroll
-  for (int w = 0; w < MW; ++w) {
-    if (32 * w > c) break;
-    const int kn = min(32, c + 1 - 32 * w);
-    for (int k = 0; k < kn; ++k) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64((bits[w] >> k) & 1u);
-      if (l == ((32 * w + k) & 63)) keep[w / 2] = m;
-    }
-  }
+  for (int e = 0; e < 32; ++e) jv[e] = e < s.topk ? row[e] : -1;
   uint64_t* dst = revmap + (((size_t)b * s.Hkv + g) * nblk) * nblk + c;
+  // two chunks at a time: their transposes are independent chains
+  for (int q = 0; 64 * q <= c; q += 2) {
+    uint64_t r[2] = {0ull, 0ull};  // indices outside 0 .. c are ignored
 #pragma unroll
-  for (int q = 0; q < MQ; ++q) {
-    const int j = 64 * q + l;
-    if (j <= c) dst[(size_t)j * nblk] = keep[q];
+    for (int e = 0; e < 32; ++e) {
+      const int j = jv[e];
+      const bool in = j >= 0 && j <= c;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) r[x] |= (in && (j >> 6) == q + x) ? 1ull << (j & 63) : 0ull;
+    }
+    // transpose: at stage h, lanes l and l ^ h exchange the h-bit halves of
+    // every 2h-bit group that the other one needs
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+      const uint64_t lo = h == 32 ? 0x00000000FFFFFFFFull : h == 16 ? 0x0000FFFF0000FFFFull
+                        : h == 8 ? 0x00FF00FF00FF00FFull : h == 4 ? 0x0F0F0F0F0F0F0F0Full
+                        : h == 2 ? 0x3333333333333333ull : 0x5555555555555555ull;
+      uint64_t p[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) p[x] = shfl_xor64(r[x], h);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        r[x] = (l & h) ? ((r[x] & ~lo) | ((p[x] & ~lo) >> h)) : ((r[x] & lo) | ((p[x] & lo) << h));
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = 64 * (q + x) + l;
+      if (j <= c) dst[(size_t)j * nblk] = r[x];
+    }
   }
 }
 
@@ -297,12 +308,7 @@ hipError_t launch_bwd_revmap(const Shape& s, const int32_t* indices, uint64_t* r
                              hipStream_t st) {
   const int nblk = s.T / kBlock;
   dim3 grid(nblk, s.Hkv, s.B);
-  if (nblk <= 128)
-    hipLaunchKernelGGL(bwd_revmap_kernel<4>, grid, dim3(64), 0, st, s, indices, revmap);
-  else if (nblk <= 256)
-    hipLaunchKernelGGL(bwd_revmap_kernel<8>, grid, dim3(64), 0, st, s, indices, revmap);
-  else  // sequences up to 65536: 1024 blocks
-    hipLaunchKernelGGL(bwd_revmap_kernel<32>, grid, dim3(64), 0, st, s, indices, revmap);
+  hipLaunchKernelGGL(bwd_revmap_kernel, grid, dim3(64), 0, st, s, indices, revmap);
   return hipGetLastError();
 }
 
