@@ -15,17 +15,22 @@
 // Here the selection work is packed instead.
 //
 // Work decomposition.  One workgroup per (64 positions = one key block, KV
-// group, batch): eight waves, each owning two column groups (4 positions x 4
-// heads each), 256 registers per lane.
-//   * Register range: each column group's window blocks (or only its own
-//     block when the window branch is off).  There the wave computes, as the
-//     general kernel does, the window branch and the selections that fall in
-//     the range, with both accumulators in registers and one exponential per
-//     element serving both branches.
-//   * Items: every other selected block j is a list of the tile's positions
-//     that chose it, four to an item (16 full MFMA columns).  The items of a
-//     block are dealt to the waves round-robin (a wave takes at most two of
-//     one block); an item's P V is added into fp32 row accumulators in LDS.
+// group, batch): sixteen waves, each owning one column group (4 positions x 4
+// heads), 128 registers per lane (a build option gives eight waves with two
+// column groups each and 256 registers).
+//   * Register range: the window blocks of the tile's first position (or
+//     only the own block when the window branch is off), the same for every
+//     column group.  There the wave computes, as the general kernel does, the
+//     window branch and the selections that fall in the range, with both
+//     accumulators in registers and one exponential per element serving both
+//     branches.  The range is software-pipelined: a period issues Q K^T of
+//     its block, then P V of the previous range block, then takes the
+//     exponentials.
+//   * Items: every selected block j before the range is a list of the tile's
+//     positions that chose it, four to an item (16 full MFMA columns).  The
+//     items of a block are dealt to the waves round-robin (a wave takes at
+//     most one of a block, two with eight waves); an item's P V is added into
+//     fp32 row accumulators in LDS.
 // Both parts use the row's fixed softmax reference (a Cauchy-Schwarz bound,
 // or the exact per-branch maxima in the rare rows where the bound is loose),
 // so a row's sum over its blocks is a plain sum: the order of the additions
@@ -33,7 +38,7 @@
 //
 // The walk.  Blocks j_begin .. own are walked once, one barrier per block.
 // Each block's image (K and V^T in MFMA fragment order, written by the pooling
-// kernel) is copied global -> LDS with 1 KB global_load_lds pieces, two per
+// kernel) is copied global -> LDS with 1 KB global_load_lds pieces, one per
 // wave, into a ring of three K slots and four V^T slots; the copy of block
 // i + 2 is issued in period i.  An item is two-stage: in the period of its
 // block the wave issues Q K^T (Q rows from the tile's copy in LDS, the item's
@@ -111,10 +116,14 @@ bool sel_compact_eligible(bool is_bf16, const Shape& s) {
          (s.W - 1) / kBlock + 2 <= kcMAXR && sel_compact_lds_bytes(s.T) <= 160 * 1024;
 }
 
-// compile-time tag of the walk's two period bodies
+// compile-time tags of the walk's period bodies
 template <bool B>
 struct RangeTag {
   static constexpr bool value = B;
+};
+template <int V>
+struct ItemsTag {
+  static constexpr int value = V;
 };
 
 __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArgs args) {
@@ -126,6 +135,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // K / V^T fragments per LDS read batch: all of them (reads first, a
   // scheduling fence, then the MFMAs) when registers allow, else pairs
   constexpr int KF = kcNW == 8 ? NFRAG : 2;
+  constexpr int KFR = KF;  // the item stages' batch in periods with the register range
   constexpr int ACC = kcACC;
   const float INF = __builtin_inff();
 
@@ -173,10 +183,15 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   float* mref = reinterpret_cast<float*>(deal + (nb + 7) / 8 * 8);  // [ROWS] selection references
 
   const int j_win0 = win_on ? max(0, t0 - W + 1) / kBlock : c_last + 1;
+  // Every column group's register range starts at the first window block of
+  // the tile's first position (the own block when the window is off), so no
+  // block of the range has items.  Where a group's window starts later, its
+  // leading range blocks are window-edge blocks, masked per element.
+  const int jr_tile = win_on ? j_win0 : own;
   const int j_begin = need_sel ? 0 : j_win0;
   const int nblk = c_last - j_begin + 1;
 
-  // Stage loads: wave w copies pieces 2 w and 2 w + 1 of the block image
+  // Stage loads: wave w copies pieces kcPPW w .. kcPPW w + kcPPW - 1 of the block image
   // (pieces 0 .. 7 are the K fragments, 8 .. 15 the V^T fragments); lane l
   // copies its 16 bytes of each piece.
   static_assert(Img::PIECES == kcPPW * NW, "pieces per wave");
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   for (int cg = 0; cg < NCG; ++cg) {
     const int C = NCG * w + cg;
     const int tf = t0 + C * NSG, tl = tf + NSG - 1;
-    jr_lo[cg] = win_on ? max(0, tf - W + 1) / kBlock : own;
+    jr_lo[cg] = jr_tile;
     jw_edge[cg] = (win_on && tl >= W) ? (tl - W) / kBlock : -1;
     float qq = 0.f, d = 0.f;
     const int r = 16 * C + col;
@@ -279,8 +294,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       if (e >= P * topk) continue;
       const int pp = e / topk, j = iv[i];
       if (j < 0) continue;
-      const int tq = t0 + (pp / NSG) * NSG;  // first position of its column group
-      const int lo = win_on ? max(0, tq - W + 1) / kBlock : tq / kBlock;
+      const int lo = jr_tile;
       if (j >= lo) {
         if (j - lo < kcMAXR) atomicOr(&selbits[pp], 1u << (j - lo));  // else not causal: never read
       } else {
@@ -421,7 +435,8 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
   // stage B of the pending items: exponentials, P V over the block's V^T
   // (vst), row sums, then the rows' accumulator update
-  auto finish_items = [&](const unsigned char* vst) __attribute__((always_inline)) {
+  auto finish_items = [&](const unsigned char* vst, auto wide_tag) __attribute__((always_inline)) {
+    constexpr int KF = decltype(wide_tag)::value ? NFRAG : KFR;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
       if (!pend[x]) continue;
@@ -432,6 +447,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       f32x4 cur[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) cur[mt] = *reinterpret_cast<const f32x4*>(rowp + 16 * mt + 4 * a);
+      const float cur_l = rowp[kcD];
       FragT vf[KF];
       if constexpr (KF == NFRAG) {
 #pragma unroll
@@ -470,13 +486,14 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           *reinterpret_cast<f32x4*>(rowp + 16 * mt + 4 * a) = o1[mt];
-        if (a == 0) rowp[kcD] += dl;
+        if (a == 0) rowp[kcD] = cur_l + dl;
       }
     }
   };
 
   // stage A of this wave's items of block bi (K fragments in kst): Q K^T
-  auto start_items = [&](int bi, const unsigned char* kst) __attribute__((always_inline)) {
+  auto start_items = [&](int bi, const unsigned char* kst, auto wide_tag) __attribute__((always_inline)) {
+    constexpr int KF = decltype(wide_tag)::value ? NFRAG : KFR;
     int has[NX], any = 0;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
@@ -513,8 +530,40 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     }
   };
 
-  // register-range work of block j for the wave's column groups
-  auto range_block = [&](int j, const unsigned char* kst, const unsigned char* vst) __attribute__((always_inline)) {
+  // Register-range work, software-pipelined over the range's blocks: in the
+  // period of block j the wave issues Q K^T of block j, then P V of block
+  // j - 1 (its P kept in registers, the block's V^T still in its ring slot),
+  // then takes the exponentials of block j while those products run, so the
+  // matrix unit and the VALU work side by side.
+  FragT psc[NCG][2], pwc[NCG][2];  // P of the previous range block (both branches)
+  int pvs[NCG], pvw[NCG];          // wave-uniform: that block's branches are active
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) { pvs[cg] = 0; pvw[cg] = 0; }
+  auto range_pv = [&](const unsigned char* vst) __attribute__((always_inline)) {
+    int any = 0;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) any |= pvs[cg] | pvw[cg];
+    if (!any) return;
+#pragma unroll
+    for (int f0 = 0; f0 < NFRAG; f0 += KF) {
+      FragT vf[KF];
+#pragma unroll
+      for (int i = 0; i < KF; ++i) vf[i] = lds_frag<T>(vst + (size_t)(f0 + i) * 1024, l);
+#pragma unroll
+      for (int i = 0; i < KF; ++i) {
+        const int mt = Img::v_mt(f0 + i), hf = Img::v_h(f0 + i);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          if (pvs[cg]) acc_s[cg][mt] = mma(acc_s[cg][mt], vf[i], psc[cg][hf]);
+          if (pvw[cg]) acc_w[cg][mt] = mma(acc_w[cg][mt], vf[i], pwc[cg][hf]);
+        }
+      }
+    }
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) { pvs[cg] = 0; pvw[cg] = 0; }
+  };
+  // block j (K fragments in kst); vprev: the V^T of block j - 1
+  auto range_block = [&](int j, const unsigned char* kst, const unsigned char* vprev) __attribute__((always_inline)) {
     bool sl[NCG], wl[NCG], act_s[NCG], act_w[NCG], act[NCG], wlow[NCG];
     bool any = false;
 #pragma unroll
@@ -522,14 +571,17 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       const bool in = j >= jr_lo[cg];  // (every column group's range ends at the own block)
       sl[cg] = in && ((sb[cg] >> (j - jr_lo[cg])) & 1u);
       act_s[cg] = __builtin_amdgcn_ballot_w64(sl[cg]) != 0;
-      act_w[cg] = in && win_on;  // when the window is on the range is exactly its blocks
+      act_w[cg] = in && win_on;  // when the window is on, the range holds its blocks (and edge blocks)
       const int tp = tpos[cg];
       wl[cg] = act_w[cg] && j * kBlock <= tp && j * kBlock + kBlock - 1 > tp - W;
       wlow[cg] = act_w[cg] && j <= jw_edge[cg];
       act[cg] = act_s[cg] || act_w[cg];
       any |= act[cg];
     }
-    if (!any) return;
+    if (!any) {
+      range_pv(vprev);
+      return;
+    }
     f32x4 st[NCG][4];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
@@ -554,16 +606,10 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       for (int i = 0; i < KF; ++i)
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg)
-          if (act[cg]) st[cg][Img::k_u(f0 + i)] = mma(st[cg][Img::k_u(f0 + i)], kf[i], qo[cg][Img::k_ks(f0 + i)]);
+          st[cg][Img::k_u(f0 + i)] = mma(st[cg][Img::k_u(f0 + i)], kf[i], qo[cg][Img::k_ks(f0 + i)]);  // (unused when inactive)
     }
-    // the first V^T fragments (all of them when registers allow) are read
-    // while the softmax runs
-    FragT vfr[KF];
-#pragma unroll
-    for (int i = 0; i < KF; ++i) vfr[i] = lds_frag<T>(vst + (size_t)i * 1024, l);
-    if constexpr (KF == NFRAG) __builtin_amdgcn_sched_barrier(0);
+    range_pv(vprev);
 
-    FragT ps[NCG][2], pw[NCG][2];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       if (!act[cg]) continue;
@@ -588,18 +634,18 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
         if (both) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            ps[cg][hf] = frag_keep(pf[hf], sl[cg]);
-            pw[cg][hf] = frag_keep(pf[hf], wl[cg]);
+            psc[cg][hf] = frag_keep(pf[hf], sl[cg]);
+            pwc[cg][hf] = frag_keep(pf[hf], wl[cg]);
           }
-          l_s[cg] += frag_sum(ps[cg][0]) + frag_sum(ps[cg][1]);
-          l_w[cg] += frag_sum(pw[cg][0]) + frag_sum(pw[cg][1]);
+          l_s[cg] += frag_sum(psc[cg][0]) + frag_sum(psc[cg][1]);
+          l_w[cg] += frag_sum(pwc[cg][0]) + frag_sum(pwc[cg][1]);
         } else {
           // one branch only: both sums are updated (the other by 0), so
           // neither accumulator is addressed through a selected pointer
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            ps[cg][hf] = pf[hf];
-            pw[cg][hf] = pf[hf];
+            psc[cg][hf] = pf[hf];
+            pwc[cg][hf] = pf[hf];
           }
           const float sp = frag_sum(pf[0]) + frag_sum(pf[1]);
           l_s[cg] += act_s[cg] ? sp : 0.f;
@@ -629,27 +675,14 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
               qw[e] = inw ? fast_exp2(x - mw) : 0.f;
             }
           }
-          ps[cg][hf] = Frag<T>::from_f32(pv);
-          pw[cg][hf] = Frag<T>::from_f32(qw);
+          psc[cg][hf] = Frag<T>::from_f32(pv);
+          pwc[cg][hf] = Frag<T>::from_f32(qw);
         }
-        if (act_s[cg]) l_s[cg] += frag_sum(ps[cg][0]) + frag_sum(ps[cg][1]);
-        if (act_w[cg]) l_w[cg] += frag_sum(pw[cg][0]) + frag_sum(pw[cg][1]);
+        if (act_s[cg]) l_s[cg] += frag_sum(psc[cg][0]) + frag_sum(psc[cg][1]);
+        if (act_w[cg]) l_w[cg] += frag_sum(pwc[cg][0]) + frag_sum(pwc[cg][1]);
       }
-    }
-#pragma unroll
-    for (int f0 = 0; f0 < NFRAG; f0 += KF) {
-      FragT vf[KF];
-#pragma unroll
-      for (int i = 0; i < KF; ++i) vf[i] = f0 == 0 ? vfr[i] : lds_frag<T>(vst + (size_t)(f0 + i) * 1024, l);
-#pragma unroll
-      for (int i = 0; i < KF; ++i) {
-        const int mt = Img::v_mt(f0 + i), hf = Img::v_h(f0 + i);
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          if (act_s[cg]) acc_s[cg][mt] = mma(acc_s[cg][mt], vf[i], ps[cg][hf]);
-          if (act_w[cg]) acc_w[cg][mt] = mma(acc_w[cg][mt], vf[i], pw[cg][hf]);
-        }
-      }
+      pvs[cg] = act_s[cg];
+      pvw[cg] = act_w[cg];
     }
   };
 
@@ -658,44 +691,44 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // of block bi - 1, the register range, stage A of the items of block bi.
   // Every path has exactly one barrier per block.
   int kslot = 0, vslot = 0;  // ring slots of block bi
-  auto period = [&](int bi, auto range_tag) __attribute__((always_inline)) {
+  auto period = [&](int bi, auto range_tag, auto items_tag) __attribute__((always_inline)) {
     constexpr bool RANGE = decltype(range_tag)::value;
+    constexpr int ITEMS = decltype(items_tag)::value;  // 0 none, 1 stage B only, 2 both stages
     if (bi + 1 < nblk) wait_vmcnt<kcPPW>();
     else wait_vmcnt<0>();
     barrier_keep_loads();  // block bi in LDS; every wave is done with block bi - 1's K and bi - 2's V^T
     if (bi + 2 < nblk) issue();
     const unsigned char* kst = kring + (size_t)kslot * kcHALF;
-    const unsigned char* vst = vring + (size_t)vslot * kcHALF;
-    if (any_pend()) finish_items(vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF);
-    if (RANGE) range_block(j_begin + bi, kst, vst);
-    start_items(bi, kst);
+    const unsigned char* vprev = vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF;
+    if (ITEMS >= 1 && any_pend()) finish_items(vprev, RangeTag<!RANGE>{});
+    if (RANGE) range_block(j_begin + bi, kst, vprev);
+    if (ITEMS == 2) {
+      start_items(bi, kst, RangeTag<!RANGE>{});
 #pragma unroll
-    for (int x = 0; x < NX; ++x) ev[x] >>= 1;
+      for (int x = 0; x < NX; ++x) ev[x] >>= 1;
+    }
     kslot = kslot + 1 == kcKSLOTS ? 0 : kslot + 1;
     vslot = (vslot + 1) & (kcVSLOTS - 1);
   };
   static_assert((kcVSLOTS & (kcVSLOTS - 1)) == 0, "V^T slots: a power of two");
 
-  // blocks before the wave's register ranges run a body without the range part
-  int split = nblk;
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) split = min(split, max(jr_lo[cg] - j_begin, 0));
-  split = __builtin_amdgcn_readfirstlane(split);
+  // Blocks before the register range run a body without the range part; the
+  // range's first period still finishes the items of the block before it,
+  // and its other periods have no item work.
+  const int split = max(jr_tile - j_begin, 0);
   int bi = 0;
   while (bi < split) {
     if ((bi & (kWave - 1)) == 0) refresh(bi);
     const int stop = min(split, (bi | (kWave - 1)) + 1);
-    for (; bi < stop; ++bi) period(bi, RangeTag<false>{});
+    for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{});
   }
-  while (bi < nblk) {
-    if ((bi & (kWave - 1)) == 0) refresh(bi);
-    const int stop = min(nblk, (bi | (kWave - 1)) + 1);
-    for (; bi < stop; ++bi) period(bi, RangeTag<true>{});
-  }
-  // stage B of the last block's items, after every wave has finished the
-  // previous block's updates
+  if (bi < nblk) period(bi++, RangeTag<true>{}, ItemsTag<1>{});
+  for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, ItemsTag<0>{});
+  // P V of the last range block, then stage B of the last block's items,
+  // after every wave has finished the previous block's updates
+  range_pv(vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF);
   barrier_keep_loads();
-  if (any_pend()) finish_items(vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF);
+  if (any_pend()) finish_items(vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF, RangeTag<false>{});
   __syncthreads();  // every accumulator update is in LDS
 
   // ------------------------------------------------------------ combine

@@ -95,6 +95,9 @@ CASES = [
     ("340m-gqa4", 512, 0.0, {"top_k": 2, "window": 1}),
     ("340m-gqa4", 64, 0.0, {"batch": 2}),
     ("340m-gqa4", 1024, 0.0, {"top_k": 32, "window": 64}),
+    # a window that is not a whole number of blocks: the column groups' windows
+    # start in different blocks, and the register range starts at the earliest
+    ("340m-gqa4", 1024, 1.0, {"window": 500}),
 ]
 
 
