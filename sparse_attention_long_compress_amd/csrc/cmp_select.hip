@@ -257,13 +257,18 @@ __global__ __launch_bounds__((K2Cfg<T, D, G>::NT), (K2Cfg<T, D, G>::MIN_WAVES_EU
 #pragma unroll
   for (int cg = 0; cg < CGW; ++cg) {
     lse2[cg] = (lsum[cg] > 0.f) ? m[cg] + __log2f(lsum[cg]) : -INFINITY;
+    // (the row coordinates pass through an opaque copy, so the Q loads'
+    // addresses are recomputed here rather than kept alive, in scratch,
+    // across pass 1)
+    int tq = tpos[cg], hq = hidx[cg];
+    asm volatile("" : "+v"(tq), "+v"(hq));
     if (o_cmp) {
       const float inv = lsum[cg] > 0.f ? 1.f / lsum[cg] : 0.f;
-      T* orow = o_cmp + (((size_t)b * s.T + tpos[cg]) * s.Hq + hidx[cg]) * D;
+      T* orow = o_cmp + (((size_t)b * s.T + tq) * s.Hq + hq) * D;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) store4(orow + mt * 16 + 4 * a, o[cg][mt] * inv);
     }
-    if (lse_cmp && a == 0) lse_cmp[((size_t)b * s.Hq + hidx[cg]) * s.T + tpos[cg]] = lse2[cg] * kLn2;
+    if (lse_cmp && a == 0) lse_cmp[((size_t)b * s.Hq + hq) * s.T + tq] = lse2[cg] * kLn2;
   }
 
   if (!do_topk) return;

@@ -738,24 +738,34 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // each wait a full memory round trip.
   const T* gates = (const T*)args.gates;
   T* out = (T*)args.out;
+  // The epilogue's row coordinates are recomputed here from values the
+  // compiler cannot see through, so the addresses of the setup's loads are not
+  // kept alive (in scratch) across the walk for reuse.
+  int tpe[NCG], he = h, cle = col, ae = a;
+  asm volatile("" : "+v"(he), "+v"(cle), "+v"(ae));
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    tpe[cg] = tpos[cg];
+    asm volatile("" : "+v"(tpe[cg]));
+  }
   float gcv[NCG], gsv[NCG], gwv[NCG];
   f32x4 ocv[NCG][MT];
   // (unconditional loads, selected afterwards: the compressed output's buffer
   // always exists, unwritten where unused, so it is never multiplied in)
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const int te = tpos[cg];
-    const T* grow = gates + (((size_t)b * s.T + te) * s.Hq + h) * 3;
+    const int te = tpe[cg];
+    const T* grow = gates + (((size_t)b * s.T + te) * s.Hq + he) * 3;
     gcv[cg] = to_f32(grow[0]);
     gsv[cg] = to_f32(grow[1]);
     gwv[cg] = to_f32(grow[2]);
-    const size_t obase = ((size_t)b * s.T + te) * q_row + (size_t)h * kcD;
+    const size_t obase = ((size_t)b * s.T + te) * q_row + (size_t)he * kcD;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ocv[cg][mt] = load4((const T*)args.o_cmp + obase + mt * 16 + 4 * a);
+    for (int mt = 0; mt < MT; ++mt) ocv[cg][mt] = load4((const T*)args.o_cmp + obase + mt * 16 + 4 * ae);
   }
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const bool ld = cmp_on && tpos[cg] >= kBlock - 1;
+    const bool ld = cmp_on && tpe[cg] >= kBlock - 1;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -766,18 +776,18 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   }
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const int r0 = 16 * (NCG * w + cg) + col;
+    const int r0 = 16 * (NCG * w + cg) + cle;
     const float* arow = accL + r0 * ACC;
     const float ls = xsum4(l_s[cg]) + (need_sel ? arow[kcD] : 0.f);
     const float lw = xsum4(l_w[cg]);
-    const int te = tpos[cg];
+    const int te = tpe[cg];
     const float iw = win_on ? gwv[cg] / lw : 0.f;
     const float ilw = win_on ? 1.f / lw : 0.f;
     const float il = need_sel ? 1.f / ls : 0.f;
-    const size_t obase = ((size_t)b * s.T + te) * q_row + (size_t)h * kcD;
+    const size_t obase = ((size_t)b * s.T + te) * q_row + (size_t)he * kcD;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int d0 = mt * 16 + 4 * a;
+      const int d0 = mt * 16 + 4 * ae;
       f32x4 res = acc_w[cg][mt] * iw + ocv[cg][mt] * gcv[cg];
       if (args.o_win) store4((T*)args.o_win + obase + d0, acc_w[cg][mt] * ilw);
       if (need_sel) {
@@ -790,9 +800,9 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       }
       store4(out + obase + d0, res);
     }
-    if (args.lse && a == 0) args.lse[((size_t)b * s.Hq + h) * s.T + te] = (mr_s[cg] + __log2f(ls)) * kLn2;
-    if (args.lse_win && a == 0)
-      args.lse_win[((size_t)b * s.Hq + h) * s.T + te] = win_on ? (mr_w[cg] + __log2f(lw)) * kLn2 : -INF;
+    if (args.lse && ae == 0) args.lse[((size_t)b * s.Hq + he) * s.T + te] = (mr_s[cg] + __log2f(ls)) * kLn2;
+    if (args.lse_win && ae == 0)
+      args.lse_win[((size_t)b * s.Hq + he) * s.T + te] = win_on ? (mr_w[cg] + __log2f(lw)) * kLn2 : -INF;
   }
 }
 
