@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     int has[NX], any = 0;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      has[x] = (int)((unsigned)ev[x] & 1u);
+      has[x] = (int)((ev[x] >> (bi & (kWave - 1))) & 1ull);
       any |= has[x];
     }
     if (!any) return;
@@ -691,22 +691,21 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // of block bi - 1, the register range, stage A of the items of block bi.
   // Every path has exactly one barrier per block.
   int kslot = 0, vslot = 0;  // ring slots of block bi
-  auto period = [&](int bi, auto range_tag, auto items_tag) __attribute__((always_inline)) {
+  // (FULL: blocks bi + 1 and bi + 2 exist, so the wait and the copy need no
+  // test: most periods before the register range)
+  auto period = [&](int bi, auto range_tag, auto items_tag, auto full_tag) __attribute__((always_inline)) {
     constexpr bool RANGE = decltype(range_tag)::value;
     constexpr int ITEMS = decltype(items_tag)::value;  // 0 none, 1 stage B only, 2 both stages
-    if (bi + 1 < nblk) wait_vmcnt<kcPPW>();
+    constexpr bool FULL = decltype(full_tag)::value;
+    if (FULL || bi + 1 < nblk) wait_vmcnt<kcPPW>();
     else wait_vmcnt<0>();
     barrier_keep_loads();  // block bi in LDS; every wave is done with block bi - 1's K and bi - 2's V^T
-    if (bi + 2 < nblk) issue();
+    if (FULL || bi + 2 < nblk) issue();
     const unsigned char* kst = kring + (size_t)kslot * kcHALF;
     const unsigned char* vprev = vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF;
     if (ITEMS >= 1 && any_pend()) finish_items(vprev, RangeTag<!RANGE>{});
     if (RANGE) range_block(j_begin + bi, kst, vprev);
-    if (ITEMS == 2) {
-      start_items(bi, kst, RangeTag<!RANGE>{});
-#pragma unroll
-      for (int x = 0; x < NX; ++x) ev[x] >>= 1;
-    }
+    if (ITEMS == 2) start_items(bi, kst, RangeTag<!RANGE>{});
     kslot = kslot + 1 == kcKSLOTS ? 0 : kslot + 1;
     vslot = (vslot + 1) & (kcVSLOTS - 1);
   };
@@ -717,13 +716,18 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // and its other periods have no item work.
   const int split = max(jr_tile - j_begin, 0);
   int bi = 0;
+  // (the range has at least one block, so every period before it has block
+  // bi + 1; all but possibly the last have bi + 2)
+  const int split_full = min(split, nblk - 2);
   while (bi < split) {
     if ((bi & (kWave - 1)) == 0) refresh(bi);
     const int stop = min(split, (bi | (kWave - 1)) + 1);
-    for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{});
+    const int stop_full = min(stop, split_full);
+    for (; bi < stop_full; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{}, RangeTag<true>{});
+    for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{}, RangeTag<false>{});
   }
-  if (bi < nblk) period(bi++, RangeTag<true>{}, ItemsTag<1>{});
-  for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, ItemsTag<0>{});
+  if (bi < nblk) period(bi++, RangeTag<true>{}, ItemsTag<1>{}, RangeTag<false>{});
+  for (; bi < nblk; ++bi) period(bi, RangeTag<true>{}, ItemsTag<0>{}, RangeTag<false>{});
   // P V of the last range block, then stage B of the last block's items,
   // after every wave has finished the previous block's updates
   range_pv(vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF);
