@@ -78,6 +78,8 @@ constexpr int kcQROW = kcD * 2;             // bytes per Q row in LDS
 constexpr int kcMAXR = 32;                  // register range of at most 32 blocks (bit set)
 constexpr int kcMAXW = 4;                   // chosen-block bitmap words: sequences up to 16384
 constexpr int kcACC = kcD + 4;              // accumulator row: 64 channels, item row sum, pad
+constexpr int kcCHUNK = 48;                 // blocks per item-table refresh: a multiple of the ring
+                                            // phases (12), at most one per lane
 // LDS layout
 constexpr int kcOFF_V = kcKSLOTS * kcHALF;
 constexpr int kcOFF_Q = kcOFF_V + kcVSLOTS * kcHALF;     // [ROWS][64] bf16, 16-byte chunks swizzled
@@ -208,6 +210,19 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     src_next += Img::BYTES;
     islot = islot + 1 == slots ? 0 : islot + 1;
   };
+  // the same with the slot known at compile time: the copy of block i goes to
+  // slot i mod 3 (K loaders) or i mod 4 (V^T loaders); PH = i mod 12.  The
+  // runtime slot is left as it was: twelve copies bring it back to itself.
+  const bool k_loader = w < NW / 2;
+  auto issue_c = [&](auto ph_tag) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_tag)::value;
+    unsigned char* dst = dst_base + (size_t)(k_loader ? PH % kcKSLOTS : PH % kcVSLOTS) * kcHALF;
+#pragma unroll
+    for (int pc = 0; pc < kcPPW; ++pc)
+      __builtin_amdgcn_global_load_lds((const void*)(src_next + pc * 1024), (void*)(dst + pc * 1024), 16, 0, 0);
+    src_next += Img::BYTES;
+  };
+  static_assert(12 % kcKSLOTS == 0 && 12 % kcVSLOTS == 0, "ring phases divide 12");
   // the first two blocks are copied while the setup runs
   if (nblk > 0) issue();
   if (nblk > 1) issue();
@@ -384,10 +399,10 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     for (int mt = 0; mt < MT; ++mt) { acc_s[cg][mt] = zero4(); acc_w[cg][mt] = zero4(); }
   }
 
-  // The wave's items of blocks bi .. bi + 63 (bi a multiple of 64): bit i of
-  // ev[x] is block j_begin + bi + i (x: the wave's x-th item of the block,
-  // when the block has more than NW items); lane i of ipos[x] holds that
-  // item's four positions.
+  // The wave's items of blocks cs .. cs + kcCHUNK - 1 (cs: the chunk's first
+  // block, a multiple of kcCHUNK): bit i of ev[x] is block j_begin + cs + i
+  // (x: the wave's x-th item of the block, when the block has more than NW
+  // items); lane i of ipos[x] holds that item's four positions.
   constexpr int NX = kcNX;
   unsigned long long ev[NX];
   unsigned ipos[NX];
@@ -492,20 +507,23 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   };
 
   // stage A of this wave's items of block bi (K fragments in kst): Q K^T
-  auto start_items = [&](int bi, const unsigned char* kst, auto wide_tag) __attribute__((always_inline)) {
+  // (evb: the event masks shifted so that bit `bit` is this block's; lane:
+  // the block's lane of ipos)
+  auto start_items = [&](const unsigned long long (&evb)[NX], int bit, int lane, const unsigned char* kst,
+                         auto wide_tag) __attribute__((always_inline)) {
     constexpr int KF = decltype(wide_tag)::value ? NFRAG : KFR;
     int has[NX], any = 0;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      has[x] = (int)((ev[x] >> (bi & (kWave - 1))) & 1ull);
+      has[x] = (int)((evb[x] >> bit) & 1ull);
       any |= has[x];
     }
     if (!any) return;
     FragT qa[NX][KS];
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      if (!has[x]) continue;
-      const unsigned pos4 = __builtin_amdgcn_readlane(ipos[x], bi & (kWave - 1));
+      if (NX > 1 && !has[x]) continue;  // (one item slot: has == any)
+      const unsigned pos4 = __builtin_amdgcn_readlane(ipos[x], lane);
       const unsigned p8 = (pos4 >> (8 * sg)) & 0xFFu;
       vB[x] = p8 != 0xFFu ? 1 : 0;
       rB[x] = vB[x] ? G * (int)p8 + hh : hh;  // unused columns read rows 0 .. 3 (finite)
@@ -526,7 +544,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
       for (int i2 = 0; i2 < KF; ++i2)
 #pragma unroll
         for (int x = 0; x < NX; ++x)
-          if (has[x]) sB[x][Img::k_u(f0 + i2)] = mma(sB[x][Img::k_u(f0 + i2)], kf[i2], qa[x][Img::k_ks(f0 + i2)]);
+          if (NX == 1 || has[x]) sB[x][Img::k_u(f0 + i2)] = mma(sB[x][Img::k_u(f0 + i2)], kf[i2], qa[x][Img::k_ks(f0 + i2)]);
     }
   };
 
@@ -691,6 +709,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // of block bi - 1, the register range, stage A of the items of block bi.
   // Every path has exactly one barrier per block.
   int kslot = 0, vslot = 0;  // ring slots of block bi
+  int cs = 0;                // first block of the item-table chunk
   // (FULL: blocks bi + 1 and bi + 2 exist, so the wait and the copy need no
   // test: most periods before the register range)
   auto period = [&](int bi, auto range_tag, auto items_tag, auto full_tag) __attribute__((always_inline)) {
@@ -705,9 +724,21 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     const unsigned char* vprev = vring + (size_t)((vslot + kcVSLOTS - 1) & (kcVSLOTS - 1)) * kcHALF;
     if (ITEMS >= 1 && any_pend()) finish_items(vprev, RangeTag<!RANGE>{});
     if (RANGE) range_block(j_begin + bi, kst, vprev);
-    if (ITEMS == 2) start_items(bi, kst, RangeTag<!RANGE>{});
+    if (ITEMS == 2) start_items(ev, bi - cs, bi - cs, kst, RangeTag<!RANGE>{});
     kslot = kslot + 1 == kcKSLOTS ? 0 : kslot + 1;
     vslot = (vslot + 1) & (kcVSLOTS - 1);
+  };
+  // a full period before the register range whose ring phase bi mod 12 = PH is
+  // known at compile time (evg: the event masks shifted by lane0 = bi - PH - cs)
+  auto period_c = [&](auto ph_tag, int lane0, const unsigned long long (&evg)[NX]) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_tag)::value;
+    wait_vmcnt<kcPPW>();
+    barrier_keep_loads();
+    issue_c(ItemsTag<(PH + 2) % 12>{});
+    const unsigned char* kst = kring + (size_t)(PH % kcKSLOTS) * kcHALF;
+    const unsigned char* vprev = vring + (size_t)((PH + kcVSLOTS - 1) % kcVSLOTS) * kcHALF;
+    if (any_pend()) finish_items(vprev, RangeTag<true>{});
+    start_items(evg, PH, lane0 + PH, kst, RangeTag<true>{});
   };
   static_assert((kcVSLOTS & (kcVSLOTS - 1)) == 0, "V^T slots: a power of two");
 
@@ -720,9 +751,29 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
   // bi + 1; all but possibly the last have bi + 2)
   const int split_full = min(split, nblk - 2);
   while (bi < split) {
-    if ((bi & (kWave - 1)) == 0) refresh(bi);
-    const int stop = min(split, (bi | (kWave - 1)) + 1);
+    cs = bi;  // a multiple of kcCHUNK, so of 12
+    refresh(bi);
+    const int stop = min(split, bi + kcCHUNK);
     const int stop_full = min(stop, split_full);
+    // twelve periods at a time with their ring slots known at compile time
+    for (; bi + 12 <= stop_full; bi += 12) {
+      const int lane0 = bi - cs;
+      unsigned long long evg[NX];
+#pragma unroll
+      for (int x = 0; x < NX; ++x) evg[x] = ev[x] >> lane0;
+      period_c(ItemsTag<0>{}, lane0, evg);
+      period_c(ItemsTag<1>{}, lane0, evg);
+      period_c(ItemsTag<2>{}, lane0, evg);
+      period_c(ItemsTag<3>{}, lane0, evg);
+      period_c(ItemsTag<4>{}, lane0, evg);
+      period_c(ItemsTag<5>{}, lane0, evg);
+      period_c(ItemsTag<6>{}, lane0, evg);
+      period_c(ItemsTag<7>{}, lane0, evg);
+      period_c(ItemsTag<8>{}, lane0, evg);
+      period_c(ItemsTag<9>{}, lane0, evg);
+      period_c(ItemsTag<10>{}, lane0, evg);
+      period_c(ItemsTag<11>{}, lane0, evg);
+    }
     for (; bi < stop_full; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{}, RangeTag<true>{});
     for (; bi < stop; ++bi) period(bi, RangeTag<false>{}, ItemsTag<2>{}, RangeTag<false>{});
   }
