@@ -98,6 +98,9 @@ CASES = [
     # a window that is not a whole number of blocks: the column groups' windows
     # start in different blocks, and the register range starts at the earliest
     ("340m-gqa4", 1024, 1.0, {"window": 500}),
+    # the packed kernel's longest sequence: 256 key blocks, so its item masks and
+    # per-block tables are at their largest and a tile walks five table chunks
+    ("340m-gqa4", 16384, 1.0, {}),
 ]
 
 
