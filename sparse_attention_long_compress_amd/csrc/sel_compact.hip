@@ -42,7 +42,7 @@
 // wave, into a ring of three K slots and four V^T slots; the copy of block
 // i + 2 is issued in period i.  An item is two-stage: in the period of its
 // block the wave issues Q K^T (Q rows from the tile's copy in LDS, the item's
-// four positions looked up once per 64 blocks); in the next period, with the
+// four positions looked up once per 48 blocks); in the next period, with the
 // MFMA results long complete, it takes the exponentials, issues P V (the
 // block's V^T still in its slot) and adds the result to the rows'
 // accumulators.  All accumulator updates of one period therefore come from
