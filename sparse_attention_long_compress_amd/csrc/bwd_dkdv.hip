@@ -504,7 +504,9 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
     FragT pf[4], sf[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      f32x4 sv[2] = {zero4(), zero4()}, dp[2] = {zero4(), zero4()};
+      // dP accumulates onto -Delta of each element's row: dP - Delta comes out of the MFMA
+      f32x4 sv[2] = {zero4(), zero4()};
+      f32x4 dp[2] = {f32x4{-dl[0], -dl[1], -dl[2], -dl[3]}, f32x4{-dl[4], -dl[5], -dl[6], -dl[7]}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const FragT kf = lds_frag<T>(kv + (size_t)(4 * ks + v) * FRAG_BYTES, l);
@@ -520,7 +522,7 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]);
-          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+          x[e] = p[e] * dp[e >> 2][e & 3];
         }
       } else {
         const int key = j * kBlock + KI::krow(v, col);
@@ -529,7 +531,7 @@ __global__ __launch_bounds__((KvCfg<T, D, G>::NT), 1) void bwd_dkdv_kernel(
           const int qi = ck * CP + (8 * a + e) / G;
           const int t = plist[qi < npos ? qi : 0];
           p[e] = kv_allowed(mode, key, t, Wn) ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
-          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+          x[e] = p[e] * dp[e >> 2][e & 3];
         }
       }
       pf[v] = Frag<T>::from_f32(p);
@@ -801,7 +803,9 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
 #pragma unroll
     for (int vv = 0; vv < 2; ++vv) {
       const int v = 2 * kh + vv;
-      f32x4 sv[2] = {zero4(), zero4()}, dp[2] = {zero4(), zero4()};
+      // dP accumulates onto -Delta of each element's row: dP - Delta comes out of the MFMA
+      f32x4 sv[2] = {zero4(), zero4()};
+      f32x4 dp[2] = {f32x4{-dl[0], -dl[1], -dl[2], -dl[3]}, f32x4{-dl[4], -dl[5], -dl[6], -dl[7]}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const FragT kf = lds_frag<T>(kv + (size_t)(4 * ks + v) * FRAG_BYTES, l);
@@ -817,7 +821,7 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]);
-          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+          x[e] = p[e] * dp[e >> 2][e & 3];
         }
       } else {
         const int key = j * kBlock + KI::krow(v, col);
@@ -826,7 +830,7 @@ __global__ __launch_bounds__((KvPairCfg<T, D, G>::NT)) void bwd_dkdv_pair_kernel
           const int qi = ck * CP + (8 * a + e) / G;
           const int t = plist[qi < npos ? qi : 0];
           p[e] = kv_allowed(mode, key, t, Wn) ? fast_exp2(sv[e >> 2][e & 3] * c1 - lr[e]) : 0.f;
-          x[e] = p[e] * (dp[e >> 2][e & 3] - dl[e]);
+          x[e] = p[e] * dp[e >> 2][e & 3];
         }
       }
       pf[vv] = Frag<T>::from_f32(p);

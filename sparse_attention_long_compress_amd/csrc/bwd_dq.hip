@@ -223,7 +223,9 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
       // S^T = K Q^T and dP^T = V dOs^T (K and V fragments in batches of FCH)
       f32x4 st[4], dp[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { st[u] = zero4(); dp[u] = zero4(); }
+      // dP^T accumulates onto -Delta (the row's, in every element of the lane's
+      // column), so dP - Delta comes out of the MFMA
+      for (int u = 0; u < 4; ++u) { st[u] = zero4(); dp[u] = f32x4{-dl, -dl, -dl, -dl}; }
 #pragma unroll
       for (int f0 = 0; f0 < NFRAG; f0 += FCH) {
         FragT kf[FCH], vf[FCH];
@@ -251,7 +253,7 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
           for (int e = 0; e < 8; ++e) {
             const int u = 2 * hf + e / 4, rr = e % 4;
             const float pr = fast_exp2(st[u][rr] * c1 - lr);
-            x[e] = pr * (dp[u][rr] - dl);
+            x[e] = pr * dp[u][rr];
           }
           dsf[hf] = Frag<T>::from_f32(x);
         }
@@ -268,7 +270,7 @@ __global__ __launch_bounds__((DqCfg<T, D, G>::NT)) void bwd_dq_kernel(
             else if constexpr (MODE == DQ_WIN) ok = key <= t && key > t - W;
             else ok = key < nvis;
             const float pr = ok ? fast_exp2(st[u][rr] * c1 - lr) : 0.f;
-            x[e] = pr * (dp[u][rr] - dl);
+            x[e] = pr * dp[u][rr];
           }
           dsf[hf] = Frag<T>::from_f32(x);
         }
