@@ -101,6 +101,9 @@ CASES = [
     # the packed kernel's longest sequence: 256 key blocks, so its item masks and
     # per-block tables are at their largest and a tile walks five table chunks
     ("340m-gqa4", 16384, 1.0, {}),
+    # the longest sequence the library accepts: 1024 key blocks (the general
+    # kernel; the compressed branch stages 16 chunks of pooled keys)
+    ("340m-gqa4", 65536, 1.0, {"n_q_heads": 4, "n_kv_heads": 1}),
 ]
 
 
