@@ -10,7 +10,7 @@
 // Delta = dOs . o_sel and dS_s = P_s (dP_s - Delta):
 //   dq = tau sum_s dS_s k_s,   dk_s = tau sum dS_s q,   dv_s = sum P_s dOs.
 //
-// B0 prep    : dOs = g_sel dO (element type), Delta (fp32), block images
+// B0 prep    : dOs = g_sel dO (element type), Delta (fp32, from that dOs), block images
 //              (K, V, K^T fragments) for B2 and B3.
 // B1 revmap  : M[b][g][j][c] = 64-bit mask of the positions of tile c (64
 //              positions) that selected block j -- one wave per (tile, group),
@@ -116,11 +116,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
     const Vec ov = *reinterpret_cast<const Vec*>(o_sel + base);
     Vec outv;
     float acc = 0.f, dg[3] = {0.f, 0.f, 0.f};
+    // Delta is taken from the dOs values the dP products use (rounded to the
+    // element type), so that dP - Delta is exactly zero where one key holds a
+    // row's whole probability and the rows of dS keep summing to ~0
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      const float x = gs * (float)dv[e];
-      outv[e] = (T)x;
-      acc += x * (float)ov[e];
+      outv[e] = (T)(gs * (float)dv[e]);
+      acc += (float)outv[e] * (float)ov[e];
       dg[1] += (float)dv[e] * (float)ov[e];
     }
     *reinterpret_cast<Vec*>(dos + base) = outv;
@@ -133,11 +135,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         const float d0 = (float)dv[e];
-        const float xw = gw * d0, xc = gc * d0;
-        ow_[e] = (T)xw;
-        oc_[e] = (T)xc;
-        accw += xw * (float)wv[e];
-        accc += xc * (float)cv[e];
+        ow_[e] = (T)(gw * d0);
+        oc_[e] = (T)(gc * d0);
+        accw += (float)ow_[e] * (float)wv[e];
+        accc += (float)oc_[e] * (float)cv[e];
         dg[0] += d0 * (float)cv[e];
         dg[2] += d0 * (float)wv[e];
       }

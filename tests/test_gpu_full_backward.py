@@ -73,10 +73,8 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,T,over", CASES)
-def test_full_backward_matches_oracle(name, T, over):
-    wl = WORKLOADS[name].with_(**over)
-    print("case", name, T, over, flush=True)
+def check_full(wl, T):
+    """Saved tensors, dq / dk / dv and the gate gradients of one workload against the oracle."""
     sv, got, ora, ref, _, f64 = run_full(wl, T)
     for nm in ("o_sel", "o_win", "o_cmp"):
         assert_close(to_np(sv[nm]), ora[nm], wl.dtype, nm)
@@ -93,6 +91,13 @@ def test_full_backward_matches_oracle(name, T, over):
     branches = ("o_cmp", "o_sel", "o_win")
     dgates_close(to_np(got[3]), ref[3], f64["dout"], [to_np(sv[n]) for n in branches],
                  [ora[n] for n in branches], wl.dtype)
+
+
+@pytest.mark.parametrize("name,T,over", CASES)
+def test_full_backward_matches_oracle(name, T, over):
+    wl = WORKLOADS[name].with_(**over)
+    print("case", name, T, over, flush=True)
+    check_full(wl, T)
 
 
 def test_full_backward_is_bitwise_reproducible():

@@ -1,0 +1,84 @@
+"""GPU parity over a seeded sweep of shapes inside the library's envelope:
+random batch, sequence length, heads per KV group, head dim, dtype, top-k and
+window, each forward compared with the fp64 oracle row by row, the selection
+backward on half of the shapes and the full backward (all branches and the
+gates) on the other half with the oracle's gradients.  The shapes are drawn once
+from a fixed seed, so the set is the same on every run."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_long_compress_amd as nsa
+from sparse_attention_long_compress_amd.synth import Workload
+from tests.nsa_cases import (assert_close, check_indices, device_inputs, gpu_forward,
+                             oracle_forward, to_np)
+from tests.test_gpu_backward import grad_close, run_both
+from tests.test_gpu_full_backward import check_full
+from tests.test_gpu_forward import LSE_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw_cases(seed=20261203):
+    # every (heads per group, head dim / dtype) pair twice, the rest drawn
+    rng = np.random.default_rng(seed)
+    cases = []
+    for rep in range(2):
+        for g in (1, 2, 4, 8, 16):
+            for d, dtype in ((64, "bf16"), (128, "bf16"), (64, "fp32")):
+                hkv = int(rng.integers(1, max(1, 16 // g) + 1))
+                T = 64 * int(rng.integers(1, 33))           # 64 .. 2048
+                cases.append(dict(batch=int(rng.integers(1, 3)), seq_len=T, n_q_heads=g * hkv,
+                                  n_kv_heads=hkv, head_dim=d, top_k=int(rng.integers(2, 33)),
+                                  window=int(rng.choice([1, 63, 64, 100, 500, 512, 777, 1024, 4096])),
+                                  dtype=dtype, qk_norm=bool(d == 128 and rng.random() < 0.5),
+                                  seed=5000 + len(cases), planted=float(rng.choice([0.0, 1.0]))))
+    return cases
+
+
+CASES = _draw_cases()
+
+
+def _wl(c):
+    return Workload("sweep", c["batch"], c["seq_len"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"],
+                    top_k=c["top_k"], window=c["window"], dtype=c["dtype"], qk_norm=c["qk_norm"],
+                    seed=c["seed"])
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"s{c['seed']}" for c in CASES])
+def test_forward_sweep(c):
+    wl = _wl(c)
+    print("case", c, flush=True)
+    dev, f64 = device_inputs(wl, seq_len=c["seq_len"], planted_sigma=c["planted"])
+    res = gpu_forward(wl, dev, want_indices=True, want_lse=True, want_o_sel=True)
+    torch.cuda.synchronize()
+    ora = oracle_forward(wl, f64, want_scores=True)
+    gi = res["indices"].cpu().numpy()
+    agree = check_indices(gi, ora, wl.top_k, scores=ora["scores"])
+    print("index agreement", agree.mean(), flush=True)
+    if not agree.all():
+        ora = oracle_forward(wl, f64, indices=gi)
+    assert_close(to_np(res["out"]), ora["out"], wl.dtype, "out")
+    assert_close(to_np(res["o_sel"]), ora["o_sel"], wl.dtype, "o_sel")
+    err = np.abs(res["lse_sel"].cpu().double().numpy() - ora["lse_sel"])
+    assert err.max() < LSE_TOL[wl.dtype], err.max()
+
+
+# the selection backward on every other shape of the sweep
+@pytest.mark.parametrize("c", CASES[::2], ids=[f"s{c['seed']}" for c in CASES[::2]])
+def test_select_bwd_sweep(c):
+    wl = _wl(c)
+    print("case", c, flush=True)
+    got, ref, *_ = run_both(wl, c["seq_len"], planted=c["planted"])
+    G = wl.n_q_heads // wl.n_kv_heads
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        grad_close(to_np(g_), r_, wl.dtype, nm, heads_per_key=1 if nm == "dq" else G)
+
+
+# the full backward (all branches, gate gradients) on the remaining shapes
+@pytest.mark.parametrize("c", CASES[1::2], ids=[f"s{c['seed']}" for c in CASES[1::2]])
+def test_full_backward_sweep(c):
+    wl = _wl(c)
+    print("case", c, flush=True)
+    check_full(wl, c["seq_len"])
