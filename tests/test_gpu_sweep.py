@@ -2,7 +2,9 @@
 random batch, sequence length, heads per KV group, head dim, dtype, top-k and
 window, each forward compared with the fp64 oracle row by row, the selection
 backward on half of the shapes and the full backward (all branches and the
-gates) on the other half with the oracle's gradients.  The shapes are drawn once
+gates) on the other half with the oracle's gradients, the skip flags on a
+third of them; and a seeded sweep of decode steps (caches of random lengths,
+skip flags).  The shapes are drawn once
 from a fixed seed, so the set is the same on every run."""
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ from tests.nsa_cases import (assert_close, check_indices, device_inputs, gpu_for
                              oracle_forward, to_np)
 from tests.test_gpu_backward import grad_close, run_both
 from tests.test_gpu_full_backward import check_full
-from tests.test_gpu_forward import LSE_TOL
+from tests.test_gpu_forward import LSE_TOL, _skip_flag_case
+from tests.test_gpu_decode import run_case as decode_case
 
 pytestmark = pytest.mark.gpu
 
@@ -82,3 +85,45 @@ def test_full_backward_sweep(c):
     wl = _wl(c)
     print("case", c, flush=True)
     check_full(wl, c["seq_len"])
+
+
+FLAG_SETS = [nsa.SKIP_CMP_OUT, nsa.SKIP_SEL, nsa.SKIP_WIN, nsa.SKIP_CMP_OUT | nsa.SKIP_SEL,
+             nsa.SKIP_CMP_OUT | nsa.SKIP_WIN, nsa.SKIP_SEL | nsa.SKIP_WIN]
+
+
+# skip flags (a skipped branch equals a zero gate) on every third shape
+@pytest.mark.parametrize("c", CASES[::3], ids=[f"s{c['seed']}" for c in CASES[::3]])
+def test_skip_flags_sweep(c):
+    wl = _wl(c)
+    flag = FLAG_SETS[c["seed"] % len(FLAG_SETS)]
+    print("case", c, "flags", flag, flush=True)
+    dev, f64 = device_inputs(wl, seq_len=c["seq_len"], planted_sigma=c["planted"])
+    _skip_flag_case(wl, dev, f64, flag)
+
+
+def _draw_decode_cases(seed=20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for g in (1, 2, 4, 8, 16):
+        for d, dtype in ((64, "bf16"), (128, "bf16"), (64, "fp32")):
+            hkv = int(rng.integers(1, max(1, 16 // g) + 1))
+            B = int(rng.integers(1, 5))
+            lmax = 64 * int(rng.integers(1, 65))           # 64 .. 4096
+            lens = sorted(int(x) for x in rng.integers(1, lmax + 1, B))
+            lens[-1] = lmax
+            flags = int(rng.choice([0, 0, 0] + FLAG_SETS[:4]))
+            cases.append(dict(batch=B, seq_len=lmax, lens=lens, n_q_heads=g * hkv, n_kv_heads=hkv,
+                              head_dim=d, top_k=int(rng.integers(2, 33)),
+                              window=int(rng.choice([1, 63, 64, 100, 500, 512, 777, 1024, 4096])),
+                              dtype=dtype, qk_norm=bool(d == 128 and rng.random() < 0.5),
+                              seed=6000 + len(cases), flags=flags))
+    return cases
+
+
+DECODE_CASES = _draw_decode_cases()
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=[f"d{c['seed']}" for c in DECODE_CASES])
+def test_decode_sweep(c):
+    wl = _wl(c)
+    decode_case(wl, c["batch"], c["seq_len"], c["lens"], seed=c["seed"], flags=c["flags"])
