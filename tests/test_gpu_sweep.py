@@ -3,8 +3,8 @@ random batch, sequence length, heads per KV group, head dim, dtype, top-k and
 window, each forward compared with the fp64 oracle row by row, the selection
 backward on half of the shapes and the full backward (all branches and the
 gates) on the other half with the oracle's gradients, the skip flags on a
-third of them; and a seeded sweep of decode steps (caches of random lengths,
-skip flags).  The shapes are drawn once
+third of them, logits 40 times larger (the exact-maximum path) on a quarter;
+and a seeded sweep of decode steps (caches of random lengths, skip flags).  The shapes are drawn once
 from a fixed seed, so the set is the same on every run."""
 import numpy as np
 import pytest
@@ -127,3 +127,27 @@ DECODE_CASES = _draw_decode_cases()
 def test_decode_sweep(c):
     wl = _wl(c)
     decode_case(wl, c["batch"], c["seq_len"], c["lens"], seed=c["seed"], flags=c["flags"])
+
+
+# logits large enough that the fixed Cauchy-Schwarz reference is too loose (the
+# exact-maximum path), every fourth shape: every saved tensor of the training
+# forward against the oracle on the oracle's index table
+@pytest.mark.parametrize("c", CASES[::4], ids=[f"s{c['seed']}" for c in CASES[::4]])
+def test_large_logits_sweep(c):
+    wl = _wl(c)
+    print("case", c, "q x 40", flush=True)
+    dev, f64 = device_inputs(wl, seq_len=c["seq_len"], planted_sigma=1.0, q_scale=40.0)
+    ora = oracle_forward(wl, f64)
+    idx = torch.from_numpy(ora["indices"]).to("cuda")
+    sv = nsa.forward_train(dev["q"], dev["k"], dev["v"], dev["gates"], top_k=wl.top_k,
+                           window=wl.window, scale=wl.scale, indices=idx)
+    torch.cuda.synchronize()
+    for nm in ("out", "o_sel", "o_win", "o_cmp"):
+        assert_close(to_np(sv[nm]), ora[nm], wl.dtype, nm)
+    for nm in ("lse_sel", "lse_win"):
+        got = sv[nm].cpu().double().numpy()
+        fin = np.isfinite(ora[nm])
+        np.testing.assert_array_equal(np.isfinite(got), fin)
+        rel = np.abs(got[fin] - ora[nm][fin]) / np.maximum(1.0, np.abs(ora[nm][fin]))
+        print(nm, "max rel", rel.max(), flush=True)
+        assert rel.max() < 2e-3, (nm, rel.max())
