@@ -40,7 +40,23 @@ def _draw_cases(seed=20261203):
     return cases
 
 
-CASES = _draw_cases()
+def _draw_long_packed_cases(seed=20261205):
+    # four heads per KV group at head_dim 64 in bf16 (the packed selection
+    # kernel) at lengths where its walk spans several 48-block item tables
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(6):
+        hkv = int(rng.integers(1, 5))
+        cases.append(dict(batch=int(rng.integers(1, 3)), seq_len=64 * int(rng.integers(49, 257)),
+                          n_q_heads=4 * hkv, n_kv_heads=hkv, head_dim=64,
+                          top_k=int(rng.integers(2, 33)),
+                          window=int(rng.choice([1, 64, 500, 512, 777, 1024, 2048])), dtype="bf16",
+                          qk_norm=False, seed=7000 + i, planted=float(rng.choice([0.0, 1.0]))))
+    return cases
+
+
+BASE = _draw_cases()
+CASES = BASE + _draw_long_packed_cases()  # (the long shapes: forward checks only)
 
 
 def _wl(c):
@@ -69,7 +85,7 @@ def test_forward_sweep(c):
 
 
 # the selection backward on every other shape of the sweep
-@pytest.mark.parametrize("c", CASES[::2], ids=[f"s{c['seed']}" for c in CASES[::2]])
+@pytest.mark.parametrize("c", BASE[::2], ids=[f"s{c['seed']}" for c in BASE[::2]])
 def test_select_bwd_sweep(c):
     wl = _wl(c)
     print("case", c, flush=True)
@@ -80,7 +96,7 @@ def test_select_bwd_sweep(c):
 
 
 # the full backward (all branches, gate gradients) on the remaining shapes
-@pytest.mark.parametrize("c", CASES[1::2], ids=[f"s{c['seed']}" for c in CASES[1::2]])
+@pytest.mark.parametrize("c", BASE[1::2], ids=[f"s{c['seed']}" for c in BASE[1::2]])
 def test_full_backward_sweep(c):
     wl = _wl(c)
     print("case", c, flush=True)
