@@ -56,7 +56,8 @@ def _draw_long_packed_cases(seed=20261205):
 
 
 BASE = _draw_cases()
-CASES = BASE + _draw_long_packed_cases()  # (the long shapes: forward checks only)
+LONG = _draw_long_packed_cases()
+CASES = BASE + LONG
 
 
 def _wl(c):
@@ -84,7 +85,7 @@ def test_forward_sweep(c):
     assert err.max() < LSE_TOL[wl.dtype], err.max()
 
 
-# the selection backward on every other shape of the sweep
+# the selection backward on every other short shape of the sweep
 @pytest.mark.parametrize("c", BASE[::2], ids=[f"s{c['seed']}" for c in BASE[::2]])
 def test_select_bwd_sweep(c):
     wl = _wl(c)
@@ -95,8 +96,8 @@ def test_select_bwd_sweep(c):
         grad_close(to_np(g_), r_, wl.dtype, nm, heads_per_key=1 if nm == "dq" else G)
 
 
-# the full backward (all branches, gate gradients) on the remaining shapes
-@pytest.mark.parametrize("c", BASE[1::2], ids=[f"s{c['seed']}" for c in BASE[1::2]])
+# the full backward (all branches, gate gradients) on the remaining short shapes and two long ones
+@pytest.mark.parametrize("c", BASE[1::2] + LONG[1:4:2], ids=[f"s{c['seed']}" for c in BASE[1::2] + LONG[1:4:2]])
 def test_full_backward_sweep(c):
     wl = _wl(c)
     print("case", c, flush=True)
