@@ -66,3 +66,24 @@ def test_noalloc_rejects_a_workspace_beyond_the_scratch_array():
     dev, _ = device_inputs(wl.with_(batch=4), seq_len=8192)
     with pytest.raises(nsa.NsaError, match="WORKSPACE"):
         _noalloc(wl, dev)
+
+
+def test_noalloc_equals_forward_over_the_shape_sweep():
+    # the sweep's shapes whose workspace fits the scratch array, one after the
+    # other (each call runs over the previous one's leftover scratch contents)
+    from tests.test_gpu_sweep import BASE, _wl
+    n = 0
+    for c in BASE:
+        wl = _wl(c)
+        dev, _ = device_inputs(wl, seq_len=c["seq_len"], planted_sigma=c["planted"])
+        p = nsa.params_for(dev["q"], dev["k"], top_k=wl.top_k, window=wl.window, scale=wl.scale)
+        if nsa.workspace_size(p) > nsa.NOALLOC_SCRATCH_BYTES:
+            continue
+        print("case noalloc", c, flush=True)
+        ref = gpu_forward(wl, dev, want_indices=True, want_lse=True, want_o_sel=True)
+        got = _noalloc(wl, dev)
+        torch.cuda.synchronize()
+        for nm in ("out", "indices", "lse_sel", "o_sel"):
+            assert torch.equal(got[nm], ref[nm]), (c["seed"], nm)
+        n += 1
+    assert n >= 20, n
