@@ -103,6 +103,18 @@ def test_select_bwd_full_size_340m():
         grad_close(to_np(g_), r_, wl.dtype, nm + "@8192")
 
 
+def test_select_bwd_longest_sequence():
+    # the longest sequence the library accepts (65536 positions, 1024 key
+    # blocks) on the bench's backward kernels (bf16, head_dim 64, four query
+    # heads per KV group), one KV group so that the oracle's scatter (one
+    # thread per batch and group) finishes in about a minute; every element
+    wl = WORKLOADS["340m-gqa4"].with_(n_q_heads=4, n_kv_heads=1)
+    print("case 340m-gqa4 65536 Hq 4 Hkv 1", flush=True)
+    got, ref, *_ = run_both(wl, 65536)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        grad_close(to_np(g_), r_, wl.dtype, nm + "@65536")
+
+
 def test_select_bwd_is_bitwise_reproducible():
     wl = WORKLOADS["340m-gqa4"]
     got, _, dev, idx, fwd = run_both(wl, 1024)
