@@ -240,6 +240,10 @@ def test_topk_matches_numpy_stable_argsort():
             chosen = list(cand[order[:m]])
             gap = S[cand[order[m - 1]]] - S[cand[order[m]]]
             np.testing.assert_allclose(r["gap"][0, 0, t], gap, rtol=0, atol=0)
+        if len(cand) <= m:
+            # every candidate is taken (exactly m of them at own = 5): no
+            # competing block, so the selection is decisive
+            assert r["gap"][0, 0, t] == np.inf
         want = sorted(([0] if own == 0 else [0, own]) + chosen)
         got = [int(x) for x in r["indices"][0, 0, t] if x >= 0]
         assert got == want
@@ -599,7 +603,9 @@ def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
     each complete block, softmax over the blocks complete at t, importance
     summed over the group's heads, blocks 0 and t // blk forced, the rest by
     (importance desc, index asc), one softmax over the selected tokens s <= t,
-    one over t - W < s <= t, outputs mixed by the gates."""
+    one over t - W < s <= t, outputs mixed by the gates.  Also returns the
+    importance of every complete block (0 past them) and the gap between the
+    m-th and (m+1)-th candidate (inf when every candidate is taken)."""
     Hq, D = q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
@@ -608,6 +614,8 @@ def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
     own, nc = t // blk, L // blk
     out = np.zeros((Hq, D))
     chosen_all = []
+    scores = np.zeros((Hkv, -(-L // blk)))
+    gaps = np.full(Hkv, np.inf)
     for g in range(Hkv):
         heads = range(g * G, (g + 1) * G)
         Kc = [K[j * blk:(j + 1) * blk, g].mean(0) for j in range(nc)]
@@ -620,6 +628,8 @@ def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
             z = np.array([tau * q[h] @ Kc[j] for j in range(nc)])
             e = np.exp(z - z.max())
             p_cmp[h] = e / e.sum()
+        for j in range(nc):
+            scores[g, j] = sum(p_cmp[h][j] for h in heads)
         forced = [0] if own == 0 else [0, own]
         cands = list(range(1, own))
         m = top_k - len(forced)
@@ -627,7 +637,9 @@ def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
             pick = cands
         else:
             imp = {j: sum(p_cmp[h][j] for h in heads) for j in cands}
-            pick = sorted(cands, key=lambda j: (-imp[j], j))[:m]
+            ranked = sorted(cands, key=lambda j: (-imp[j], j))
+            pick = ranked[:m]
+            gaps[g] = imp[ranked[m - 1]] - imp[ranked[m]]
         chosen = sorted(forced + pick)
         chosen_all.append(chosen + [-1] * (top_k - len(chosen)))
         sel_keys = [s for j in chosen for s in range(j * blk, (j + 1) * blk) if s <= t]
@@ -639,7 +651,7 @@ def _decode_by_enumeration(q, K, V, gates, L, top_k, W, blk=64):
                 return (e / e.sum()) @ np.array([V[s, g] for s in keys])
             o_cmp = sum(p_cmp[h][j] * Vc[j] for j in range(nc)) if nc else np.zeros(D)
             out[h] = gates[h, 0] * o_cmp + gates[h, 1] * attend(sel_keys) + gates[h, 2] * attend(win_keys)
-    return out, np.array(chosen_all)
+    return out, np.array(chosen_all), scores, gaps
 
 
 def test_decode_matches_per_query_enumeration():
@@ -652,9 +664,14 @@ def test_decode_matches_per_query_enumeration():
     gates = rng.random((B, Hq, 3))
     got = oracle.decode(q, kc, vc, gates, lens, top_k=top_k, window=W)
     for b, L in enumerate(lens):
-        ref, idx = _decode_by_enumeration(q[b], kc[b, :L], vc[b, :L], gates[b], L, top_k, W)
+        ref, idx, sc, gp = _decode_by_enumeration(q[b], kc[b, :L], vc[b, :L], gates[b], L, top_k, W)
         np.testing.assert_allclose(got["out"][b], ref, atol=1e-12, rtol=1e-10)
         assert np.array_equal(got["indices"][b], idx), (L, got["indices"][b], idx)
+        # the importance the selection ranks, and the gap the GPU tests use
+        # to tell decisive rows from near-ties
+        np.testing.assert_allclose(got["scores"][b, :, :sc.shape[1]], sc, atol=1e-13, rtol=0)
+        assert np.all(got["scores"][b, :, sc.shape[1]:] == 0.0)
+        np.testing.assert_allclose(got["gap"][b], gp, atol=1e-13, rtol=0)
 
 
 def test_decode_is_independent_of_cache_past_the_length():
