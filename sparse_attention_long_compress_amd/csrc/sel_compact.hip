@@ -456,6 +456,9 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
     for (int x = 0; x < NX; ++x) {
       if (!pend[x]) continue;
       pend[x] = 0;
+      // the period waits for the longest item chain, which is stage B's: its
+      // wave issues ahead of the other waves of its SIMD until the update is out
+      __builtin_amdgcn_s_setprio(3);
       float* rowp = accL + rB[x] * ACC;
       // every LDS read of the stage (the rows' current sums, the block's V^T
       // fragments) is issued first; the exponentials overlap their latency
@@ -503,6 +506,7 @@ __global__ __launch_bounds__(kcNT, 1) void sel_compact_kernel(Shape s, SelWinArg
           *reinterpret_cast<f32x4*>(rowp + 16 * mt + 4 * a) = o1[mt];
         if (a == 0) rowp[kcD] = cur_l + dl;
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
